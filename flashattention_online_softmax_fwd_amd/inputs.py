@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module holds no attention arithmetic: it only draws random numbers and
+rounds them to the input dtype.  The tests hand the very same tensors to the
+HIP library and to the fp64 oracle, which is the only thing the two sides
+share.
+
+Recipe: ``numpy.random.default_rng(seed)`` draws Q, K and V (in that order) as
+float32 standard normals of shape [B, Hq, N, d], [B, Hkv, N, d], [B, Hkv, N, d];
+Q is then multiplied by ``q_mult``; bf16 workloads round to bfloat16 with
+round-to-nearest-even (``torch.Tensor.to``).  The oracle reads the rounded
+values upcast exactly to float64.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str            # "f32" or "bf16"
+    causal: bool
+    q_mult: float = 1.0
+    scale: float | None = None   # None: 1/sqrt(d)
+    seed: int = 0
+    oracle_rows: int | None = None   # sampled rows for the oracle (None: all)
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """4*B*Hq*N^2*d, halved when causal (the metric's convention)."""
+        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O and LSE written once; no N x N term."""
+        return (self.B * self.N * self.d * self.esize * (2 * self.Hq + 2 * self.Hkv)
+                + 4 * self.B * self.Hq * self.N)
+
+
+# The five workloads of the method's contract, plus the scale-1 overflow stress.
+WORKLOADS = {
+    "c1_f32_n256_d64": Workload("c1_f32_n256_d64", 1, 1, 1, 256, 64, "f32", False, seed=1001),
+    "c2_bf16_n2048_d64": Workload("c2_bf16_n2048_d64", 4, 16, 16, 2048, 64, "bf16", False, seed=1002),
+    "c3_bf16_n4096_d128_causal": Workload("c3_bf16_n4096_d128_causal", 2, 32, 32, 4096, 128, "bf16",
+                                          True, seed=1003),
+    "c4_bf16_gqa_n8192_d128_causal": Workload("c4_bf16_gqa_n8192_d128_causal", 1, 32, 8, 8192, 128,
+                                              "bf16", True, seed=1004),
+    "c5_bf16_n32768_d128_causal_q12": Workload("c5_bf16_n32768_d128_causal_q12", 1, 8, 8, 32768, 128,
+                                               "bf16", True, q_mult=12.0, seed=1005, oracle_rows=512),
+    "c5s_bf16_n4096_d128_causal_q12_scale1": Workload("c5s_bf16_n4096_d128_causal_q12_scale1", 1, 8, 8,
+                                                      4096, 128, "bf16", True, q_mult=12.0, scale=1.0,
+                                                      seed=1006),
+}
+
+BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
+
+
+def torch_dtype(dtype: str):
+    if dtype == "f32":
+        return torch.float32
+    if dtype == "bf16":
+        return torch.bfloat16
+    raise ValueError("unknown dtype %r" % (dtype,))
+
+
+def make_qkv(B, Hq, Hkv, N, d, dtype="bf16", seed=0, q_mult=1.0):
+    """Seeded Q, K, V as CPU torch tensors in the input dtype."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
+    td = torch_dtype(dtype)
+    return (torch.from_numpy(q).to(td), torch.from_numpy(k).to(td), torch.from_numpy(v).to(td))
+
+
+def workload_inputs(w: Workload):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.q_mult)
+
+
+def sample_rows(w: Workload, count: int, seed: int | None = None):
+    """Sorted flat row ids (b*Hq + h)*N + i drawn without replacement.
+
+    The first row of the first head and the last row of the last head always
+    replace the first two draws, so both ends of the causal triangle are covered.
+    """
+    total = w.B * w.Hq * w.N
+    count = min(count, total)
+    rng = np.random.default_rng((w.seed + 1) if seed is None else seed)
+    rows = rng.choice(total, size=count, replace=False)
+    if count >= 2:
+        first = 0
+        last = total - 1
+        rows = rows[~np.isin(rows, [first, last])]
+        rows = np.concatenate([[first, last], rows[: count - 2]])
+    return np.sort(rows.astype(np.int64))
