@@ -1,0 +1,94 @@
+"""ctypes binding of libfa.so: the C ABI of include/fa.h, name for name.
+
+Argument marshalling only.  ``import torch`` comes first so that libfa binds
+to the HIP runtime torch has already loaded (both carry the soname
+libamdhip64.so.7): one runtime per process, and torch's stream handles are
+valid for libfa.  Loading fails loudly when the library is not built; there is
+no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must precede loading libfa; see module docstring)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
+
+# name -> (restype, argtypes), mirroring include/fa.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]
+SIGNATURES = {
+    "fa_fwd": (_I, _FWD_ARGS),
+    "fa_fwd_tiled": (_I, _FWD_ARGS + [_I, _I]),
+    "fa_tile_shapes": (_I, [_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), _I]),
+    "fa_error_string": (ctypes.c_char_p, [_I]),
+    "fa_last_error": (ctypes.c_char_p, []),
+    "fa_abi_version": (_I, []),
+}
+
+_lib = None
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+def load():
+    """Load libfa.so once; raise LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(
+                "libfa.so is not built (%s); run `python -c 'import __graft_entry__ as g; g.build()'`"
+                % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream):
+    return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+
+
+def fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, block_m, block_n):
+    return load().fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream,
+                               block_m, block_n)
+
+
+def fa_tile_shapes(dtype, d):
+    """List of (block_m, block_n) compiled for (dtype, d); the first is the default."""
+    lib = load()
+    n = lib.fa_tile_shapes(dtype, d, None, None, 0)
+    if n < 0:
+        return []
+    bm = (ctypes.c_int * n)()
+    bn = (ctypes.c_int * n)()
+    lib.fa_tile_shapes(dtype, d, bm, bn, n)
+    return list(zip(bm, bn))
+
+
+def fa_error_string(code):
+    return load().fa_error_string(code).decode()
+
+
+def fa_last_error():
+    return load().fa_last_error().decode()
+
+
+def fa_abi_version():
+    return load().fa_abi_version()
