@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward TFLOP/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+One step is one fa_fwd call over the whole workload (every query row of every
+head): the full hot path, one kernel launch.  Inputs are seeded synthetic
+tensors already resident in HBM when the timed region starts.  W untimed steps,
+then exactly K timed steps between two device synchronisations.
+
+Printed: one JSON line (rank 0, the only rank).  ``value`` is 4*B*Hq*N^2*d
+(halved when causal) per step over the timed wall time, in TFLOP/s.
+``roofline`` prices the kernel's average launch duration, measured with HIP
+events on the stream it runs on, against MI355X's dense bf16 MFMA peak.
+``cpu_baseline`` times the fp64 oracle on a bounded, seeded sample of the same
+workload's query rows on this host's cores and compares those rows with the
+GPU output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (and % of MFMA peak) at bf16 N=4096 d=128 causal"
+
+# MI355X published dense peaks (no sparsity): 256 CUs at 2.4 GHz.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBPS = 8000.0
+
+KERNEL_SOURCES = {
+    "bf16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_bf16.hip",
+    "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_hash(dtype: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str, dtype: str):
+    """HBM bytes per launch from committed rocprofv3 counters, or None.
+
+    None when no counters were taken for this workload, or when the kernel
+    source changed since they were (its hash is stored next to them).
+    """
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = table.get(workload)
+    if not entry or entry.get("kernel_source_sha256") != kernel_hash(dtype):
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def time_gpu(fa, q, k, v, w, steps, warmup):
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    for _ in range(warmup):
+        fa.forward(q, k, v, causal=w.causal, scale=w.softmax_scale, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fa.forward(q, k, v, causal=w.causal, scale=w.softmax_scale, out=o, lse=lse)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, per_launch_ms, o, lse
+
+
+def cpu_baseline(w, q, k, v, o, lse, budget_s):
+    """Time the fp64 oracle on seeded sample rows until about budget_s seconds."""
+    import numpy as np
+
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+    from oracle import fa_oracle
+
+    total = w.B * w.Hq * w.N
+    order = fin.sample_rows(w, total if total <= 1 << 20 else 1 << 20, seed=w.seed + 7)
+    np.random.default_rng(w.seed + 8).shuffle(order)
+    qh, kh, vh = (fa_oracle._as_f64(t) for t in (q, k, v))   # exact upcast, outside the timing
+    done, spent, chunk = [], 0.0, 64
+    outs, lses = [], []
+    pos = 0
+    while spent < budget_s and pos < len(order):
+        rows = np.sort(order[pos:pos + chunk])
+        pos += len(rows)
+        t0 = time.perf_counter()
+        ro, rl = fa_oracle.attention(qh, kh, vh, causal=w.causal, scale=w.softmax_scale, rows=rows)
+        spent += time.perf_counter() - t0
+        done.append(rows)
+        outs.append(ro)
+        lses.append(rl)
+        chunk = min(chunk * 2, 4096)
+    rows = np.concatenate(done)
+    ro = np.concatenate(outs)
+    rl = np.concatenate(lses)
+    flops = fa_oracle.row_flops(w.N, w.d, w.causal, rows)
+    go = o.reshape(-1, w.d)[torch_index(rows, o.device)].float().cpu().numpy()
+    gl = lse.reshape(-1)[torch_index(rows, o.device)].cpu().numpy()
+    atol, rtol = (1e-2, 2e-2) if w.dtype == "bf16" else (1e-5, 0.0)
+    ok = bool(np.all(np.abs(go - ro) <= atol + rtol * np.abs(ro))
+              and np.all(np.abs(gl - rl) <= atol + rtol * np.abs(rl)))
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": fa_oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d seeded query rows of %s (%.3g of its %.3g flops), fp64 three-pass oracle, %.1f s"
+                  % (len(rows), w.name, flops, w.flops, spent),
+        "seconds": spent,
+        "rows": int(len(rows)),
+        "gpu_matches_oracle_on_sample": ok,
+        "max_abs_err_o": float(np.abs(go - ro).max()),
+        "max_abs_err_lse": float(np.abs(gl - rl).max()),
+    }
+
+
+def torch_index(rows, device):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.long, device=device)
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_budget):
+    import torch
+
+    import flashattention_online_softmax_fwd_amd as fa
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+
+    fa.load_library()
+    w = fin.WORKLOADS[name]
+    q, k, v = fin.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    torch.cuda.synchronize()
+    wall, per_ms, o, lse = time_gpu(fa, qd, kd, vd, w, steps, warmup)
+    ms_step = wall * 1e3 / steps
+    tflops = w.flops * steps / wall / 1e12
+    avg_launch_ms = sum(per_ms) / len(per_ms)
+    achieved = w.flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/K/V, numpy default_rng(%d)%s)"
+                % (w.seed, ", Q x %g" % w.q_mult if w.q_mult != 1.0 else ""),
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.softmax_scale, "dtype": w.dtype,
+                   "flops_per_step": w.flops},
+        "frac_of_peak": tflops / peak,
+        "hbm_gbps": w.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic_for(w.name, w.dtype),
+            "kernel": "fa::fwd_%s_kernel" % w.dtype,
+            "avg_launch_ms": avg_launch_ms,
+            "min_launch_ms": min(per_ms),
+            "algorithmic_flops_per_launch": w.flops,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+        },
+    }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, o, lse, cpu_budget)
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="one of inputs.WORKLOADS (default: the metric's)")
+    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run torch.neg over 256 MiB of float32 three times: a plain "
+                         "kernel that reads and writes known byte counts, for scaling HBM counters")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the shard plan is in "
+              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+    if args.all:
+        for name in fin.WORKLOADS:
+            print(json.dumps(run_workload(name, args.steps, args.warmup, False, 0.0)), flush=True)
+        return 0
+    name = args.workload or fin.BENCH_WORKLOAD
+    rec = run_workload(name, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+    if args.copy_calibration:
+        x = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        rec["copy_calibration"] = {"kernel": "torch.neg float32", "read_bytes": x.numel() * 4,
+                                   "write_bytes": y.numel() * 4, "launches": 3}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

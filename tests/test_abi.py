@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: libfa.so loads, exports what include/fa.h declares, and
+rejects bad arguments on the host before any HIP call (so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+PKG = os.path.join(ROOT, "flashattention_online_softmax_fwd_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from flashattention_online_softmax_fwd_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from flashattention_online_softmax_fwd_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
+                          "fa_last_error", "fa_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_binding_mirrors_the_header():
+    from flashattention_online_softmax_fwd_amd import _lib
+    assert sorted(_lib.SIGNATURES) == declared_functions()
+
+
+def test_library_never_allocates_device_memory():
+    out = subprocess.run(["nm", "-D", "--undefined-only", os.path.join(PKG, "libfa.so")],
+                         capture_output=True, text=True, check=True).stdout
+    for sym in ("hipMalloc", "hipFree", "hipMallocAsync", "hipExtMallocWithFlags", "hipHostMalloc",
+                "hipMemcpy", "hipDeviceSynchronize", "hipStreamSynchronize"):
+        assert not re.search(r"\b%s\b" % sym, out), sym
+
+
+def test_product_path_does_not_touch_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower() or f == "inputs.py", f
+    src = open(os.path.join(PKG, "inputs.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+
+
+def test_version_and_error_strings(lib):
+    assert lib.fa_abi_version() == 1
+    assert lib.fa_error_string(0) == b"ok"
+    assert lib.fa_error_string(1) == b"invalid argument"
+    assert lib.fa_error_string(2) == b"unsupported request"
+    assert lib.fa_error_string(3) == b"HIP runtime error"
+    assert lib.fa_error_string(99) == b"unknown error code"
+
+
+def test_tile_shapes(lib):
+    from flashattention_online_softmax_fwd_amd import _lib
+    for dtype in (0, 1):
+        for d in (64, 128):
+            shapes = _lib.fa_tile_shapes(dtype, d)
+            assert len(shapes) >= 2 and len(set(shapes)) == len(shapes)
+    assert lib.fa_tile_shapes(1, 96, None, None, 0) == -1
+    assert lib.fa_tile_shapes(7, 64, None, None, 0) == -1
+
+
+P = 0x10000   # a 16-byte-aligned non-null value; never dereferenced by the checks below
+
+
+def call(lib, q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000, B=1, Hq=2, Hkv=1,
+         N=16, d=64, causal=0, scale=0.125, dtype=1, stream=None):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(q=P + 8), 1),                                   # misaligned
+    (dict(B=-1), 1), (dict(N=-5), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1),
+    (dict(Hq=3, Hkv=2), 1), (dict(d=0), 1), (dict(causal=2), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1), (dict(scale=3e38), 1),
+    (dict(dtype=5), 1), (dict(dtype=2), 2), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(o=P), 1),                                       # o overlaps q
+    (dict(lse=P + 0x300010), 1),                          # lse overlaps o
+])
+def test_invalid_arguments_are_rejected_before_any_hip_call(lib, kw, code):
+    assert call(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_empty_problems_return_ok_without_touching_pointers(lib):
+    assert call(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+    assert call(lib, q=0, k=0, v=0, o=0, lse=0, N=0) == 0
+
+
+def test_unknown_tile_is_unsupported(lib):
+    args = (P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, 1, 2, 1, 16, 64, 0, 0.125, 1, None)
+    assert lib.fa_fwd_tiled(*args, 96, 64) == 2
+    assert lib.fa_fwd_tiled(*args, 0, 64) == 1
+    assert lib.fa_fwd_tiled(*args, -128, 64) == 1
+
+
+def test_python_wrapper_checks_before_the_library():
+    import torch
+
+    import flashattention_online_softmax_fwd_amd as fa
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x)                     # CPU tensors are refused
+    with pytest.raises(ValueError):
+        fa.forward(torch.zeros(4, 64), x, x)    # wrong rank
