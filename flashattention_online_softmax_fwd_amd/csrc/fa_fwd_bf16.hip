@@ -1,34 +1,47 @@
 // fa_fwd_bf16.hip -- bf16 FlashAttention forward for gfx950 (CDNA4, MI355X).
 //
-// One workgroup owns BM query rows of one (batch, query head) and walks the key
-// tiles of its K/V head in order (query blocks outer, key blocks inner: kbwen.com
-// FlashAttention feed, "More than two blocks").  Each wave owns 32 query rows.
+// One workgroup (4 waves) owns 128 query rows of one (batch, query head) and
+// walks the key tiles of its K/V head in order: query blocks outer, key blocks
+// inner (kbwen.com FlashAttention feed, "More than two blocks").  Each wave owns
+// 32 query rows; two workgroups share a CU, so two waves share each SIMD and one
+// wave's exponentials overlap the other's matrix products.
 //
 // Per key tile of BN keys, for each wave:
-//   S^T = K_tile Q_w^T        v_mfma_f32_32x32x16_bf16, fp32 accumulate
-//   t   = S^T * scale*log2(e), -inf where masked (causal j > i, or j >= N)
-//   m'  = max(m, rowmax t)     in-lane max over 32 keys, then one lane swap
-//   a   = exp2(m - m'),  P = exp2(t - m')      (a row with no finite score yet
-//                                               uses 0 as its reference: the guard)
-//   l   = a*l + rowsum P,  O^T = a*O^T + V_tile^T P^T     (P rounded to bf16)
+//   S^T = K_tile Q_w^T          v_mfma_f32_32x32x16_bf16, fp32 accumulate
+//   -inf where masked           only on tiles that cross the diagonal or the N tail
+//   mx  = rowmax S^T * c        c = scale * log2(e); one lane-half swap per row
+//   if mx > m + 8: m' = mx, a = exp2(m - m'), l *= a, O *= a      (lazy rescale)
+//   P   = exp2(S^T * c - m)     one FMA and one v_exp_f32 per score
+//   l  += rowsum P,  O^T += V_tile^T P^T        (P rounded to bf16)
 // and after the last tile O = O^T / l, LSE = (m + log2 l) * ln 2.
-// The update is the one the pages derive (mbrenndoerfer.com "Online Softmax
-// Computation", its five steps; spicyshark.co online-softmax lesson, "From
-// softmax to attention" and "The implementation"), in base 2: exp(x) =
-// exp2(x*log2 e), so the scale and log2(e) fold into one multiplier.
 //
-// Why the scores are computed transposed: the 32x32 MFMA leaves lane L holding
-// one column of its output.  With K as the A operand and Q as the B operand
-// that column is one query row, so the row max and row sum are in-lane except
-// for one exchange between lane halves, and the bf16-rounded probabilities are
-// already where the PV MFMA wants its B operand: no LDS round trip for P.
+// This is the update the pages derive (mbrenndoerfer.com "Online Softmax
+// Computation", its update equations and five steps; spicyshark.co online-softmax
+// lesson, "The idea", "From softmax to attention" and "The implementation") in
+// base 2, with one liberty the mathematics allows: the reference m is moved only
+// when the row maximum has grown by more than 2^8.  Between moves l and O are
+// both measured against the same, slightly stale m, so every term carries the
+// same factor and u / l is unchanged; P stays below 2^8, far from any overflow.
+// A row whose tiles so far held no finite score keeps m = -inf and adds nothing
+// (the pages' guard for a fully masked block).  l sums the bf16-rounded P, the
+// very weights the PV product uses.
 //
-// LDS, double-buffered: K tile [BN][D+8] (row-major, 16-byte pad) and V^T tile
-// [D][BN+8].  V is transposed in registers while it is staged (4 keys x 8 dims per
-// thread, v_perm_b32), and the keys of each group of 16 are stored in the order
-// that makes each lane's 8 PV operands one contiguous 16-byte read.
+// Why the scores are transposed: lane L of a 32x32 MFMA output holds one column.
+// With K as the A operand that column is one query row, so the row max and sum
+// are in-lane except for one exchange between lane halves, and the rounded P is
+// already the B operand of the PV product: P never goes through LDS.
+//
+// LDS, double-buffered: K and V tiles, both row-major [BN][D] with 16-byte chunks
+// XOR-swizzled per row, filled straight from HBM by buffer_load_dwordx4 ... lds
+// (rows past N read as zero: the buffer range ends at the last key).  The PV A
+// operand (V^T) comes from ds_read_b64_tr_b16, which transposes 4 keys x 16 dims
+// across each group of 16 lanes, so V needs no transposition anywhere.  The four
+// tile buffers are separate arrays and the key loop is unrolled by two, so every
+// access names its buffer statically: the compiler can then see that reading
+// one buffer does not wait for the loads still landing in the other.
 #include "fa_kernels.h"
 
+#include <float.h>
 #include <stdint.h>
 
 namespace fa {
@@ -36,53 +49,99 @@ namespace fa {
 typedef __bf16 bf16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+
+#define FA_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kRescaleSlack = 8.0f;   // log2 units: P may grow to 2^8 before m moves
 
-// Position of key `key4` (a multiple of 4) inside the V^T row: within each group
-// of 16 keys, key 16g + 8a + 4b + c is stored at 16g + 8b + 4a + c.  The lane
-// half `hi` of a PV MFMA then reads keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the
-// group -- exactly the keys its score registers hold -- as one 16-byte vector.
-__device__ __forceinline__ int vt_pos(int key4)
+// XOR mask for the 16-byte chunks of K/V tile row r.  Chosen so that both LDS read
+// patterns are free of bank conflicts: 16 consecutive rows at one logical chunk
+// (the K operand) and 4 consecutive rows x 4 consecutive chunks (the V operand).
+template <int D>
+__device__ __forceinline__ int swz(int r)
 {
-    return (key4 & ~15) | ((key4 & 4) << 1) | ((key4 & 8) >> 1);
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);   // D == 64: 8 chunks, 2 rows per bank row
 }
 
+// Reductions over the two lane halves, which hold the same query row.
+__device__ __forceinline__ float lane_half_max(float x)
+{
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ float lane_half_sum(float x)
+{
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <bool V>
+struct Flag {
+    static constexpr bool value = V;
+};
+
+template <int V>
+struct Int {
+    static constexpr int value = V;
+};
+
 template <int D, int BM, int BN, bool CAUSAL>
-__global__ void __launch_bounds__(BM * 2)
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const FwdParams p)
 {
-    constexpr int NW = BM / 32;            // waves, 32 query rows each
-    constexpr int NT = NW * 64;            // threads
-    constexpr int KS = D + 8;              // K tile row stride (elements)
-    constexpr int VS = BN + 8;             // V^T tile row stride (elements)
-    constexpr int DK = D / 16;             // MFMA k-steps over the head dimension
-    constexpr int ST = BN / 32;            // 32-key score tiles per K/V tile
-    constexpr int DT = D / 32;             // 32-dim output tiles
-    constexpr int KCH = BN * D / 8 / NT;   // 16-byte K chunks per thread per tile
-    constexpr int VUNITS = (BN / 4) * (D / 8);   // V staging units: 4 keys x 8 dims
-    constexpr int VPT = (VUNITS + NT - 1) / NT;
-    static_assert(BM % 32 == 0 && BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert((BN * D / 8) % NT == 0, "K tile must split evenly over the threads");
+    static_assert(BM == 128, "four waves of 32 query rows");
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(BN % 32 == 0, "key tile");
+    constexpr int NW = BM / 32;
+    constexpr int ROWB = D * 2;                 // bytes per K/V row
+    constexpr int TILEB = BN * ROWB;            // bytes per K or V tile
+    constexpr int LOADS = TILEB / 1024;         // 1 KiB wave-loads per tile (each of K, V)
+    constexpr int DK = D / 16;                  // k-steps of the score product
+    constexpr int ST = BN / 32;                 // 32-key score tiles per key tile
+    constexpr int DT = D / 32;                  // 32-dim output tiles
+    static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) bf16 sk[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) bf16 sv[2][D * VS];
+    __shared__ __attribute__((aligned(1024))) char k_lds0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
     const int N = p.N;
     const int bhc = p.B * p.Hq;
+    const int nqt = p.n_qtiles;
     const int bid = blockIdx.x;
-    // Causal: the longest rows first, so the tail of the grid is short work.
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - bid / bhc) : (bid / bhc);
-    const int bh = bid % bhc;
+    int bh, qt;
+    if (p.xcd_map) {
+        // Blocks go to the 8 XCDs round-robin.  Give each XCD a contiguous run of heads
+        // (so its L2 holds few K/V heads at a time), each head's tiles longest first.
+        const int xcd = bid & 7;
+        const int k = bid >> 3;
+        bh = xcd * (bhc >> 3) + k / nqt;
+        const int t = k % nqt;
+        qt = CAUSAL ? nqt - 1 - t : t;
+    } else {
+        bh = bid % bhc;
+        qt = CAUSAL ? nqt - 1 - bid / bhc : bid / bhc;
+    }
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;
     const int hk = hq / p.group;
     const bf16* __restrict__ Qh = (const bf16*)p.q + (size_t)bh * N * D;
-    const bf16* __restrict__ Kh = (const bf16*)p.k + (size_t)(b * p.Hkv + hk) * N * D;
-    const bf16* __restrict__ Vh = (const bf16*)p.v + (size_t)(b * p.Hkv + hk) * N * D;
+    const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
+    const char* Vh = (const char*)p.v + (size_t)(b * p.Hkv + hk) * N * ROWB;
+    // Buffer ranges end at the head's last key: loads past it return zeros.
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, N * ROWB, 0x00020000);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -91,89 +150,79 @@ fwd_bf16_kernel(const FwdParams p)
     const int hi = lane >> 5;
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * 32;
-    const int my_q = qw0 + l32;            // the query row this lane's columns belong to
+    const int my_q = qw0 + l32;
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    // Q as the B operand: lane holds dims 16kk + 8hi .. +7 of its query row.
+    // Q as the B operand of S^T = K Q^T: dims 16kk + 8hi .. +7 of this lane's row.
+    // A negative scale is folded into Q's sign so that c > 0 below; a zero scale
+    // becomes the smallest normal float, which leaves every exp2 argument at 0.
+    const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
+    const unsigned qflip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
     bf16x8 qf[DK];
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-        qf[kk] = (my_q < N) ? *(const bf16x8*)(Qh + (size_t)my_q * D + 16 * kk + 8 * hi)
-                            : __builtin_bit_cast(bf16x8, zero4);
+    for (int kk = 0; kk < DK; ++kk) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (my_q < N) raw = *(const u32x4*)(Qh + (size_t)my_q * D + 16 * kk + 8 * hi);
+        raw ^= qflip;
+        qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    // Per-lane LDS byte offsets of the K operand: row 32t + l32, logical chunk 2kk + hi.
+    const int kx = swz<D>(l32);
+    int koff[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) koff[kk] = l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
+    // V operand (transposed read): lane (group G, index 4j + s) addresses row
+    // 32t + 16u + 8r + 4(G>>1) + j and dims 32dt + 16(G&1) + 4s .. +3.
+    const int G = lane >> 4;
+    const int jj = (lane >> 2) & 3;
+    const int ss = lane & 3;
+    int voff[2][DT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 8 * r + 4 * (G >> 1) + jj;
+        const int w = swz<D>(row);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
+            voff[r][dt] = row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+        }
+    }
 
     f32x16 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = -INFINITY;   // running max, log2 domain of the scaled score
-    float l_run = 0.f;         // running sum over this lane half's keys
+    float m_ref = -INFINITY;   // exp reference, log2 units of the scaled score
+    float l_run = 0.f;         // sum of P over this lane half's keys, against m_ref
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    u32x4 kr[KCH];
-    u32x4 vr[VPT][4];
-
-    auto gload = [&](int j) {
+    // One tile of K and V into buffer BUF, straight from HBM into LDS.
+    auto issue_loads = [&](int j, auto bufsel) {
+        constexpr int BUF = decltype(bufsel)::value;
+        char* kdst = BUF == 0 ? k_lds0 : k_lds1;
+        char* vdst = BUF == 0 ? v_lds0 : v_lds1;
         const int kv0 = j * BN;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            const int key = c / (D / 8);
-            const int col = (c % (D / 8)) * 8;
-            const int gk = kv0 + key;
-            kr[i] = (gk < N) ? *(const u32x4*)(Kh + (size_t)gk * D + col) : zero4;
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + i * NT;
-            if ((VUNITS % NT) == 0 || u < VUNITS) {
-                const int quad = u % (BN / 4);
-                const int ch = u / (BN / 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int gk = kv0 + 4 * quad + r;
-                    vr[i][r] = (gk < N) ? *(const u32x4*)(Vh + (size_t)gk * D + 8 * ch) : zero4;
-                }
-            }
+        for (int i = 0; i < LOADS / NW; ++i) {
+            const int ii = wave + i * NW;                 // which 1 KiB slice of the tile
+            const int off = ii * 1024 + 16 * lane;        // this lane's physical bytes
+            const int row = off / ROWB;
+            const int chunk = ((off % ROWB) >> 4) ^ swz<D>(row);
+            const unsigned src = (unsigned)((kv0 + row) * ROWB + 16 * chunk);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kdst + ii * 1024), 16, src, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vdst + ii * 1024), 16, src, 0, 0, 0);
         }
     };
 
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            const int key = c / (D / 8);
-            const int col = (c % (D / 8)) * 8;
-            *(u32x4*)&sk[buf][key * KS + col] = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + i * NT;
-            if ((VUNITS % NT) == 0 || u < VUNITS) {
-                const int quad = u % (BN / 4);
-                const int ch = u / (BN / 4);
-                const int pos = vt_pos(4 * quad);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // dims 8ch+2e (low halves) and 8ch+2e+1 (high halves) of keys 0..3
-                    u32x2 ev, od;
-                    ev[0] = __builtin_amdgcn_perm(vr[i][1][e], vr[i][0][e], 0x05040100u);
-                    ev[1] = __builtin_amdgcn_perm(vr[i][3][e], vr[i][2][e], 0x05040100u);
-                    od[0] = __builtin_amdgcn_perm(vr[i][1][e], vr[i][0][e], 0x07060302u);
-                    od[1] = __builtin_amdgcn_perm(vr[i][3][e], vr[i][2][e], 0x07060302u);
-                    *(u32x2*)&sv[buf][(8 * ch + 2 * e) * VS + pos] = ev;
-                    *(u32x2*)&sv[buf][(8 * ch + 2 * e + 1) * VS + pos] = od;
-                }
-            }
-        }
-    };
-
-    auto compute = [&](int j, int buf) {
+    auto compute = [&](int j, auto bufsel, auto masked) {
+        constexpr int BUF = decltype(bufsel)::value;
+        constexpr bool MASK = decltype(masked)::value;
         const int kv0 = j * BN;
-        if (CAUSAL && kv0 > qw0 + 31) return;     // every key of the tile is masked for this wave
+        const char* kb = BUF == 0 ? k_lds0 : k_lds1;
+        const char* vb = BUF == 0 ? v_lds0 : v_lds1;
 
         f32x16 s[ST];
 #pragma unroll
@@ -182,74 +231,95 @@ fwd_bf16_kernel(const FwdParams p)
             for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const bf16x8 a = *(const bf16x8*)&sk[buf][(32 * t + l32) * KS + 16 * kk + 8 * hi];
+                const bf16x8 a = *(const FA_LDS bf16x8*)(kb + 32 * t * ROWB + koff[kk]);
                 s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[t], 0, 0, 0);
             }
         }
 
         // lane holds keys kv0 + 32t + 8(r/4) + 4hi + r%4 of query my_q
-        const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < ST; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[t][r] * p.scale_log2;
-                if (need_mask) {
-                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (key >= N || (CAUSAL && key > my_q)) x = -INFINITY;
-                }
-                s[t][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // no finite score yet
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-
-        float rs = 0.f;
-        bf16x8 pb[ST][2];
-#pragma unroll
-        for (int t = 0; t < ST; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(s[t][r] - m_use);
-                rs += e;
-                pb[t][r >> 3][r & 7] = (bf16)e;
-            }
-        l_run = l_run * alpha + rs;
-
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        if constexpr (MASK) {
+            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (kv0 + 4 * hi);   // last visible, relative
 #pragma unroll
             for (int t = 0; t < ST; ++t)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const bf16x8 a =
-                        *(const bf16x8*)&sv[buf][(32 * dt + l32) * VS + 32 * t + 16 * u + 8 * hi];
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][u], o[dt], 0, 0, 0);
+                for (int r = 0; r < 16; ++r)
+                    if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int t = 0; t < ST; ++t)
+#pragma unroll
+            for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+        mx = lane_half_max(mx) * c;
+
+        // lazy rescale: move the reference only when the max has grown past the slack
+        const bool grow = mx > m_ref + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;   // nothing finite yet: P = 0
+
+        bf16x8 pb[ST][2];
+        float ls0 = 0.f, ls1 = 0.f;
+        const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+        for (int t = 0; t < ST; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    bf16x2 pair;
+                    pair[0] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e], c, -m_use));
+                    pair[1] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e + 1], c, -m_use));
+                    pb[t][u][e] = pair[0];
+                    pb[t][u][e + 1] = pair[1];
+                    if (e & 2) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls1, false);
+                    else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls0, false);
+                }
+        l_run += ls0 + ls1;
+
+#pragma unroll
+        for (int t = 0; t < ST; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const char* vrow = vb + (32 * t + 16 * u) * ROWB;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vrow + voff[0][dt]));
+                    const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vrow + voff[1][dt]));
+                    const i16x8 both = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[t][u],
+                                                                   o[dt], 0, 0, 0);
                 }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const bool more = j + 1 < ntiles;
-        if (more) gload(j + 1);
-        compute(j, j & 1);
-        if (more) lstore((j + 1) & 1);
-        __syncthreads();
+    // Tile j in buffer CUR: wait for it, start tile j + 1 into the other buffer, use tile j.
+    auto step = [&](int j, auto cursel) {
+        constexpr int CUR = decltype(cursel)::value;
+        __syncthreads();                     // tile j landed; the other buffer is free
+        if (j + 1 < ntiles) issue_loads(j + 1, Int<1 - CUR>{});
+        const int kv0 = j * BN;
+        if (CAUSAL && kv0 > qw0 + 31) return;                   // wholly above this wave's diagonal
+        const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
+        if (need_mask) compute(j, cursel, Flag<true>{});
+        else compute(j, cursel, Flag<false>{});
+    };
+
+    issue_loads(0, Int<0>{});
+    for (int j = 0; j < ntiles; j += 2) {
+        step(j, Int<0>{});
+        if (j + 1 < ntiles) step(j + 1, Int<1>{});
     }
 
     // epilogue: O = u / l, LSE = m + ln l
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = lane_half_sum(l_run);
     if (my_q < N) {
         const float inv = 1.f / l_tot;
         bf16* Orow = (bf16*)p.o + (size_t)bh * N * D + (size_t)my_q * D;
@@ -259,11 +329,10 @@ fwd_bf16_kernel(const FwdParams p)
             for (int g = 0; g < 4; ++g) {
                 bf16x4 w;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (bf16)(o[dt][4 * g + c] * inv);
+                for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dt][4 * g + e] * inv);
                 *(bf16x4*)(Orow + 32 * dt + 8 * g + 4 * hi) = w;
             }
-        if (hi == 0)
-            p.lse[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -273,21 +342,20 @@ fwd_bf16_kernel(const FwdParams p)
     template __global__ void fwd_bf16_kernel<D, BM, BN, false>(const FwdParams);  \
     template __global__ void fwd_bf16_kernel<D, BM, BN, true>(const FwdParams);
 FA_BF16_INSTANTIATE(128, 128, 64)
-FA_BF16_INSTANTIATE(128, 128, 128)
-FA_BF16_INSTANTIATE(128, 64, 64)
-FA_BF16_INSTANTIATE(64, 128, 64)
+FA_BF16_INSTANTIATE(128, 128, 32)
 FA_BF16_INSTANTIATE(64, 128, 128)
-FA_BF16_INSTANTIATE(64, 64, 64)
+FA_BF16_INSTANTIATE(64, 128, 64)
 
 namespace {
 
 template <int D, int BM, int BN, bool CAUSAL>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((long long)p.B * p.Hq * p.n_qtiles);
+    const long long grid = (long long)p.B * p.Hq * p.n_qtiles;
     FwdParams args = p;
+    args.xcd_map = ((p.B * p.Hq) % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, BM, BN, CAUSAL>, dim3(grid),
+    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, BM, BN, CAUSAL>, dim3((unsigned)grid),
                            dim3(BM * 2), kargs, 0, stream);
 }
 
@@ -302,11 +370,9 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
 // The first shape listed for each head dimension is the default.
 const KernelEntry kBf16Kernels[] = {
     FA_BF16_ENTRY(128, 128, 64),
-    FA_BF16_ENTRY(128, 128, 128),
-    FA_BF16_ENTRY(128, 64, 64),
-    FA_BF16_ENTRY(64, 128, 64),
+    FA_BF16_ENTRY(128, 128, 32),
     FA_BF16_ENTRY(64, 128, 128),
-    FA_BF16_ENTRY(64, 64, 64),
+    FA_BF16_ENTRY(64, 128, 64),
 };
 const int kNumBf16Kernels = sizeof(kBf16Kernels) / sizeof(kBf16Kernels[0]);
 

@@ -107,6 +107,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.group = Hq / Hkv;
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)folded;
+    p.xcd_map = 0;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;

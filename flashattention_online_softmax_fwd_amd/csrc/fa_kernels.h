@@ -17,6 +17,7 @@ struct FwdParams {
     int group;       // Hq / Hkv: query heads per K/V head
     int n_qtiles;    // ceil(N / block_m)
     float scale_log2;  // scale * log2(e): scores go straight to the exp2 domain
+    int xcd_map;       // 1: block order spreads whole heads over the 8 XCDs (set by the launcher)
 };
 
 using Launcher = hipError_t (*)(const FwdParams&, hipStream_t);
