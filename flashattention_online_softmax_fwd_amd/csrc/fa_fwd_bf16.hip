@@ -83,6 +83,16 @@ __device__ __forceinline__ float lane_half_sum(float x)
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// The tile barrier.  Loads that write LDS directly (buffer_load ... lds) count in
+// vmcnt, and a workgroup barrier does not by itself wait for them, so each wave
+// first waits for its own tile loads to land; after the barrier every wave's loads
+// have, and the whole tile is visible.
+__device__ __forceinline__ void tile_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
+    __syncthreads();
+}
+
 template <bool V>
 struct Flag {
     static constexpr bool value = V;
@@ -199,32 +209,35 @@ fwd_bf16_kernel(const FwdParams p)
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kv_end + BN - 1) / BN;
 
-    // One tile of K and V into buffer BUF, straight from HBM into LDS.
-    auto issue_loads = [&](int j, auto bufsel) {
-        constexpr int BUF = decltype(bufsel)::value;
-        char* kdst = BUF == 0 ? k_lds0 : k_lds1;
-        char* vdst = BUF == 0 ? v_lds0 : v_lds1;
-        const int kv0 = j * BN;
+    // Tile j of K (or V) into buffer BUF, straight from HBM into LDS.
+    auto issue_k = [&](int j, auto bufsel) {
+        char* dst = decltype(bufsel)::value == 0 ? k_lds0 : k_lds1;
 #pragma unroll
         for (int i = 0; i < LOADS / NW; ++i) {
             const int ii = wave + i * NW;                 // which 1 KiB slice of the tile
             const int off = ii * 1024 + 16 * lane;        // this lane's physical bytes
             const int row = off / ROWB;
             const int chunk = ((off % ROWB) >> 4) ^ swz<D>(row);
-            const unsigned src = (unsigned)((kv0 + row) * ROWB + 16 * chunk);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kdst + ii * 1024), 16, src, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vdst + ii * 1024), 16, src, 0, 0, 0);
+            const unsigned src = (unsigned)((j * BN + row) * ROWB + 16 * chunk);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(dst + ii * 1024), 16, src, 0, 0, 0);
+        }
+    };
+    auto issue_v = [&](int j, auto bufsel) {
+        char* dst = decltype(bufsel)::value == 0 ? v_lds0 : v_lds1;
+#pragma unroll
+        for (int i = 0; i < LOADS / NW; ++i) {
+            const int ii = wave + i * NW;
+            const int off = ii * 1024 + 16 * lane;
+            const int row = off / ROWB;
+            const int chunk = ((off % ROWB) >> 4) ^ swz<D>(row);
+            const unsigned src = (unsigned)((j * BN + row) * ROWB + 16 * chunk);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(dst + ii * 1024), 16, src, 0, 0, 0);
         }
     };
 
-    auto compute = [&](int j, auto bufsel, auto masked) {
-        constexpr int BUF = decltype(bufsel)::value;
-        constexpr bool MASK = decltype(masked)::value;
-        const int kv0 = j * BN;
-        const char* kb = BUF == 0 ? k_lds0 : k_lds1;
-        const char* vb = BUF == 0 ? v_lds0 : v_lds1;
-
-        f32x16 s[ST];
+    // S^T of one key tile from the K buffer BUF.
+    auto s_tile = [&](f32x16 (&s)[ST], auto bufsel) {
+        const char* kb = decltype(bufsel)::value == 0 ? k_lds0 : k_lds1;
 #pragma unroll
         for (int t = 0; t < ST; ++t) {
 #pragma unroll
@@ -235,38 +248,36 @@ fwd_bf16_kernel(const FwdParams p)
                 s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[t], 0, 0, 0);
             }
         }
+    };
 
-        // lane holds keys kv0 + 32t + 8(r/4) + 4hi + r%4 of query my_q
-        if constexpr (MASK) {
-            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (kv0 + 4 * hi);   // last visible, relative
-#pragma unroll
-            for (int t = 0; t < ST; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
-        }
-        float mx = s[0][0];
+    // -inf for keys this lane's row may not see (only ever needed on a wave's last tile).
+    auto mask_tile = [&](f32x16 (&s)[ST], int j) {
+        const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (j * BN + 4 * hi);   // relative last key
 #pragma unroll
         for (int t = 0; t < ST; ++t)
 #pragma unroll
-            for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-        mx = lane_half_max(mx) * c;
+            for (int r = 0; r < 16; ++r)
+                if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
+    };
 
+    // Online-softmax update for one tile of scores: returns the rescale factor for O
+    // (1 where the reference did not move) and whether any row of the wave moved.
+    auto softmax = [&](f32x16 (&s)[ST], bf16x8 (&pb)[ST][2], float& alpha) -> bool {
+        float mx0 = s[0][0], mx1 = s[0][1];
+#pragma unroll
+        for (int t = 0; t < ST; ++t)
+#pragma unroll
+            for (int r = (t == 0 ? 2 : 0); r < 16; r += 2) {
+                mx0 = fmaxf(mx0, s[t][r]);
+                mx1 = fmaxf(mx1, s[t][r + 1]);
+            }
+        const float mx = lane_half_max(fmaxf(mx0, mx1)) * c;
         // lazy rescale: move the reference only when the max has grown past the slack
         const bool grow = mx > m_ref + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        }
+        const float m_new = grow ? mx : m_ref;
+        alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        m_ref = m_new;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;   // nothing finite yet: P = 0
-
-        bf16x8 pb[ST][2];
         float ls0 = 0.f, ls1 = 0.f;
         const bf16x2 one = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
@@ -283,8 +294,20 @@ fwd_bf16_kernel(const FwdParams p)
                     if (e & 2) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls1, false);
                     else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls0, false);
                 }
-        l_run += ls0 + ls1;
+        l_run = l_run * alpha + (ls0 + ls1);
+        return __builtin_amdgcn_ballot_w64(grow) != 0;
+    };
 
+    auto rescale_o = [&](float alpha) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    };
+
+    // O^T += V_tile^T P^T from the V buffer BUF.
+    auto pv = [&](const bf16x8 (&pb)[ST][2], auto bufsel) {
+        const char* vb = decltype(bufsel)::value == 0 ? v_lds0 : v_lds1;
 #pragma unroll
         for (int t = 0; t < ST; ++t)
 #pragma unroll
@@ -300,22 +323,43 @@ fwd_bf16_kernel(const FwdParams p)
                 }
     };
 
-    // Tile j in buffer CUR: wait for it, start tile j + 1 into the other buffer, use tile j.
-    auto step = [&](int j, auto cursel) {
-        constexpr int CUR = decltype(cursel)::value;
-        __syncthreads();                     // tile j landed; the other buffer is free
-        if (j + 1 < ntiles) issue_loads(j + 1, Int<1 - CUR>{});
-        const int kv0 = j * BN;
-        if (CAUSAL && kv0 > qw0 + 31) return;                   // wholly above this wave's diagonal
-        const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
-        if (need_mask) compute(j, cursel, Flag<true>{});
-        else compute(j, cursel, Flag<false>{});
+    // Software pipeline, per wave: while tile j's softmax runs on the VALU, tile j+1's
+    // scores run on the MFMA unit; then tile j's PV product.  Iteration j reads K_{j+1}
+    // and V_j and loads K_{j+2} and V_{j+1}, so K runs one tile ahead of V.  A wave's only
+    // masked tile is its last one (the tile holding its diagonal, or the N tail), so the
+    // steady-state iteration carries no mask code.
+    const int my_last = CAUSAL ? min(ntiles - 1, (qw0 + 31) / BN) : ntiles - 1;
+    // Scores of tile j live in sa for even j and in sb for odd j: no copies between tiles.
+    f32x16 sa[ST], sb[ST];
+
+    auto iter = [&](int j, auto par, f32x16 (&s_cur)[ST], f32x16 (&s_nxt)[ST]) {
+        constexpr int P = decltype(par)::value;     // j & 1: V_j in V buffer P, K_{j+1} in K buffer 1-P
+        tile_barrier();                            // K_{j+1} and V_j landed; K_j and V_{j-1} are free
+        if (j + 2 < ntiles) issue_k(j + 2, Int<P>{});
+        if (j + 1 < ntiles) issue_v(j + 1, Int<1 - P>{});
+        if (j > my_last) return;                   // this wave's rows are done
+        bf16x8 pb[ST][2];
+        float alpha;
+        bool any;
+        if (j < my_last) {
+            s_tile(s_nxt, Int<1 - P>{});
+            any = softmax(s_cur, pb, alpha);
+        } else {
+            if ((CAUSAL && j * BN + BN - 1 > qw0) || (j * BN + BN > N)) mask_tile(s_cur, j);
+            any = softmax(s_cur, pb, alpha);
+        }
+        if (any) rescale_o(alpha);
+        pv(pb, Int<P>{});
     };
 
-    issue_loads(0, Int<0>{});
+    issue_k(0, Int<0>{});
+    issue_v(0, Int<0>{});
+    if (ntiles > 1) issue_k(1, Int<1>{});
+    tile_barrier();
+    s_tile(sa, Int<0>{});                          // every wave sees key 0
     for (int j = 0; j < ntiles; j += 2) {
-        step(j, Int<0>{});
-        if (j + 1 < ntiles) step(j + 1, Int<1>{});
+        iter(j, Int<0>{}, sa, sb);
+        if (j + 1 < ntiles) iter(j + 1, Int<1>{}, sb, sa);
     }
 
     // epilogue: O = u / l, LSE = m + ln l
@@ -343,8 +387,8 @@ fwd_bf16_kernel(const FwdParams p)
     template __global__ void fwd_bf16_kernel<D, BM, BN, true>(const FwdParams);
 FA_BF16_INSTANTIATE(128, 128, 64)
 FA_BF16_INSTANTIATE(128, 128, 32)
-FA_BF16_INSTANTIATE(64, 128, 128)
 FA_BF16_INSTANTIATE(64, 128, 64)
+FA_BF16_INSTANTIATE(64, 128, 32)
 
 namespace {
 
@@ -371,8 +415,8 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
 const KernelEntry kBf16Kernels[] = {
     FA_BF16_ENTRY(128, 128, 64),
     FA_BF16_ENTRY(128, 128, 32),
-    FA_BF16_ENTRY(64, 128, 128),
     FA_BF16_ENTRY(64, 128, 64),
+    FA_BF16_ENTRY(64, 128, 32),
 };
 const int kNumBf16Kernels = sizeof(kBf16Kernels) / sizeof(kBf16Kernels[0]);
 

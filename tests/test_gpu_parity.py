@@ -190,6 +190,8 @@ def test_every_tile_shape(fa, oracle, dtype, d, causal):
     assert len(shapes) >= 2
     for tile in shapes:
         parity(fa, oracle, 1, 4, 2, 419, d, dtype, causal, seed=7, tile=tile)
+        # many key tiles per query tile: every tile barrier must see the whole tile
+        parity(fa, oracle, 1, 2, 1, 1531, d, dtype, causal, seed=8, tile=tile)
 
 
 # ------------------------------------------------------------- closed forms

@@ -1,0 +1,58 @@
+"""Static checks on the gfx950 code the kernels compile to (CPU only: hipcc here).
+
+The bf16 kernel stages K/V tiles with loads that write LDS directly
+(buffer_load ... lds).  Those loads count in vmcnt, and a workgroup barrier does
+not by itself wait for them: every s_barrier must therefore follow an s_waitcnt
+that includes vmcnt(0), or a wave could pass the barrier while its part of the
+next tile is still landing and other waves would read stale data.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "flashattention_online_softmax_fwd_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+
+
+@pytest.fixture(scope="module")
+def bf16_asm(tmp_path_factory):
+    if not HIPCC:
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("isa") / "bf16.s")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+                    "--offload-device-only", "-S", os.path.join(CSRC, "fa_fwd_bf16.hip"), "-o", out],
+                   check=True, capture_output=True)
+    return open(out).read()
+
+
+def kernels(asm):
+    for name in re.findall(r"^(_ZN2fa15fwd_bf16_kernel\S+):", asm, re.M):
+        i = asm.index(name + ":")
+        j = asm.index(".Lfunc_end", i)
+        body = [l.strip() for l in asm[i:j].splitlines()]
+        yield name, [l for l in body if l and not l.startswith((";", "."))]
+
+
+def test_every_barrier_waits_for_lds_dma(bf16_asm):
+    found = 0
+    for name, ins in kernels(bf16_asm):
+        found += 1
+        assert any(x.startswith("buffer_load_dwordx4") and x.endswith("lds") for x in ins), name
+        for n, x in enumerate(ins):
+            if x.startswith("s_barrier"):
+                assert ins[n - 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[n - 1], (name, n, ins[n - 1])
+    assert found >= 8
+
+
+def test_no_packed_fp32_and_no_scratch(bf16_asm):
+    for name, ins in kernels(bf16_asm):
+        assert not any(x.startswith(("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")) for x in ins), name
+    # the default tile shapes must not spill
+    for name, ins in kernels(bf16_asm):
+        if "Li128ELi64E" in name:
+            assert not any(x.startswith("scratch_") for x in ins), name
