@@ -199,8 +199,10 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU clock ramps up over the first tens of milliseconds of sustained MFMA work,
+    # so the default warm-up is long enough (~65 ms at the default workload) to reach it.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None, help="one of inputs.WORKLOADS (default: the metric's)")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
