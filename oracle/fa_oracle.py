@@ -50,6 +50,12 @@ def _load(path: str | None = None):
                                     ctypes.c_double,
                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
         lib.fa_ref_rows.restype = ctypes.c_int
+        lib.fa_ref_rows_kv.argtypes = [dp, dp, dp, dp, dp,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
+        lib.fa_ref_rows_kv.restype = ctypes.c_int
         lib.fa_ref_num_threads.argtypes = []
         lib.fa_ref_num_threads.restype = ctypes.c_int
         _libs[path] = lib
@@ -109,6 +115,84 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, rows=No
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return o, lse
+
+
+def attention_kv(q, k, v, causal: bool = False, scale: float | None = None, k_range=None,
+                 rows=None, lib_path: str | None = None):
+    """Exact attention of Nq queries against Nk keys, over a key range, in fp64.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d].  causal: key j is visible to query i
+    iff j <= i + (Nk - Nq).  k_range = (k_lo, k_hi) keeps only keys in [k_lo, k_hi)
+    (default: all).  A row with no visible key in the range gets the empty state,
+    o = 0 and lse = -inf.  rows: flat ids (b*Hq + h)*Nq + i.
+
+    Returns (o, lse) shaped like ``attention``'s, with Nq in place of N.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    k_lo, k_hi = (0, Nk) if k_range is None else (int(k_range[0]), int(k_range[1]))
+    if rows is None:
+        o = np.empty((B, Hq, Nq, d), dtype=np.float64)
+        lse = np.empty((B, Hq, Nq), dtype=np.float64)
+        rows_p = None
+        nrows = B * Hq * Nq
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        nrows = rows_a.size
+        o = np.empty((nrows, d), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rows_p = rows_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = _load(lib_path).fa_ref_rows_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                        k_lo, k_hi, rows_p, nrows)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Merge partial attention states of disjoint key sets, in fp64.
+
+    o_parts [S, ..., d] and lse_parts [S, ...]: state s in normalised form
+    (o = acc / l, lse = m + ln l; lse = -inf for an empty state).  Each state is
+    read as (m, l, acc) = (lse, 1, o), the same state measured against m + ln l,
+    and the S states are folded with the pages' merge (``online_model.merge``:
+    take the larger max, rescale each side by exp(its max - that max), add;
+    spicyshark.co lesson, "From softmax to attention" and "Check yourself").
+    Returns (o, lse) of the union; a row whose states are all empty gives o = 0,
+    lse = -inf.
+    """
+    from oracle import online_model   # the pinned fp64 model of the pages' update
+
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    S = o_parts.shape[0]
+    d = o_parts.shape[-1]
+    if lse_parts.shape != o_parts.shape[:-1]:
+        raise ValueError("lse_parts must be o_parts without its last axis")
+    flat_o = o_parts.reshape(S, -1, d)
+    flat_l = lse_parts.reshape(S, -1)
+    R = flat_o.shape[1]
+    out_o = np.zeros((R, d), dtype=np.float64)
+    out_l = np.full((R,), -np.inf, dtype=np.float64)
+    for r in range(R):
+        state = (-np.inf, 0.0, np.zeros(d))
+        for s in range(S):
+            m_s = flat_l[s, r]
+            part = (m_s, 1.0, flat_o[s, r]) if m_s > -np.inf else (-np.inf, 0.0, np.zeros(d))
+            state = online_model.merge(state, part)
+        m, l, acc = state
+        if l > 0.0:
+            out_o[r] = np.asarray(acc) / l
+            out_l[r] = m + np.log(l)
+    return out_o.reshape(o_parts.shape[1:]), out_l.reshape(lse_parts.shape[1:])
 
 
 def row_flops(N: int, d: int, causal: bool, rows) -> float:

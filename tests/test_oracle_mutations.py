@@ -22,21 +22,25 @@ MUTANTS = {
     "no_max_anywhere": [("l += exp(s[j] - m);", "l += exp(s[j]);"),
                         ("const double w = exp(s[j] - m) / l;", "const double w = exp(s[j]) / l;")],
     "min_as_reference": [("if (s[j] > m) m = s[j];", "if (s[j] < m || m == -INFINITY) m = s[j];")],
-    "causal_excludes_diagonal": [("causal ? i + 1 : N", "causal ? i : N")],
-    "causal_one_key_too_many": [("causal ? i + 1 : N", "causal ? (i + 2 < N ? i + 2 : N) : N")],
-    "causal_ignored": [("causal ? i + 1 : N", "N")],
+    "causal_excludes_diagonal": [("causal ? i + (Nk - Nq) : Nk - 1", "causal ? i + (Nk - Nq) - 1 : Nk - 1")],
+    "causal_one_key_too_many": [("causal ? i + (Nk - Nq) : Nk - 1", "causal ? i + (Nk - Nq) + 1 : Nk - 1")],
+    "causal_ignored": [("causal ? i + (Nk - Nq) : Nk - 1", "Nk - 1")],
+    "causal_offset_dropped": [("causal ? i + (Nk - Nq) : Nk - 1", "causal ? i : Nk - 1")],
+    "range_start_ignored": [("const int j_lo = k_lo;", "const int j_lo = 0;")],
+    "range_end_ignored": [("const int j_hi = last + 1 < k_hi ? last + 1 : k_hi;", "const int j_hi = last + 1;")],
+    "empty_range_lse_zero": [("*lse_out = -INFINITY;\n        return;", "*lse_out = 0.0;\n        return;")],
     "gqa_modulo_map": [("const int hk = h / group;", "const int hk = h % Hkv;")],
     "lse_in_log2": [("*lse_out = m + log(l);", "*lse_out = m + log2(l);")],
     "lse_drops_max": [("*lse_out = m + log(l);", "*lse_out = log(l);")],
     "scale_dropped": [("s[j] = scale * dot;", "s[j] = dot;")],
     "scores_transposed": [("const double* qi = q + row * d;",
-                           "const double* qi = k + ((int64_t)b * Hkv + hk) * N * d + (int64_t)i * d;"),
-                          ("const double* kh = k + ((int64_t)b * Hkv + hk) * N * d;",
-                           "const double* kh = q + ((int64_t)b * Hq + h) * N * d;")],
+                           "const double* qi = k + ((int64_t)b * Hkv + hk) * Nk * d + (int64_t)i * d;"),
+                          ("const double* kh = k + ((int64_t)b * Hkv + hk) * Nk * d;",
+                           "const double* kh = q + ((int64_t)b * Hq + h) * Nq * d;")],
     "key_index_reversed": [("const double* kj = kh + (int64_t)j * d;",
-                            "const double* kj = kh + (int64_t)(nvis - 1 - j) * d;")],
+                            "const double* kj = kh + (int64_t)(j_hi - 1 - (j - j_lo)) * d;")],
     "values_reversed": [("const double* vj = vh + (int64_t)j * d;",
-                         "const double* vj = vh + (int64_t)(nvis - 1 - j) * d;")],
+                         "const double* vj = vh + (int64_t)(j_hi - 1 - (j - j_lo)) * d;")],
     "weights_not_normalised": [("const double w = exp(s[j] - m) / l;", "const double w = exp(s[j] - m);")],
     "weight_sign_flipped": [("const double w = exp(s[j] - m) / l;", "const double w = exp(m - s[j]) / l;")],
     "dot_drops_last_term": [("for (t = 0; t < d; ++t) dot += qi[t] * kj[t];",
@@ -113,7 +117,37 @@ def check_sdpa(lib):
     return ok
 
 
-CHECKS = [check_p1, check_p4_prefixes, check_p2, check_overflow, check_sdpa]
+def _run_kv(lib, scores, values, n_query, k_range, causal=False):
+    """The embedded example with only the last n_query rows as queries, keys cut to k_range."""
+    q, k, v = _embed(scores, values)
+    o, lse = fa_oracle.attention_kv(q[:, :, -n_query:], k, v, causal=causal, scale=1.0,
+                                    k_range=k_range, lib_path=lib)
+    return o[0, 0], lse[0, 0]
+
+
+def check_two_blocks(lib):
+    """kbwen.com 'Two blocks': each block's own state, and the output of the first alone."""
+    o1, l1 = _run_kv(lib, [1.0, 3.0, 5.0, 2.0], [10.0, 20.0, 30.0, 40.0], 1, (0, 2))
+    o2, l2 = _run_kv(lib, [1.0, 3.0, 5.0, 2.0], [10.0, 20.0, 30.0, 40.0], 1, (2, 4))
+    return (abs(o1[0, 0] - 18.81) <= 0.005 and abs(math.exp(l1[0] - 3.0) - 1.1353) <= 5e-5
+            and abs(math.exp(l2[0] - 5.0) - 1.0498) <= 5e-5
+            and abs(o2[0, 0] * math.exp(l2[0] - 5.0) - 31.9915) <= 5e-4)
+
+
+def check_trailing_queries(lib):
+    """The last two positions of the five-score example as queries: the causal prefixes 4 and 5."""
+    o, _ = _run_kv(lib, [1.0, 3.0, 2.0, 5.0, 4.0], [10.0, 20.0, 30.0, 40.0, 50.0], 2, (0, 5), causal=True)
+    return bool(np.allclose(o[:, 0], [36.88, 39.95], atol=0.005))
+
+
+def check_empty_range(lib):
+    """Row 0 of a causal square problem sees no key in [3, 5): the empty state."""
+    o, lse = _run_kv(lib, [1.0, 3.0, 2.0, 5.0, 4.0], [10.0, 20.0, 30.0, 40.0, 50.0], 5, (3, 5), causal=True)
+    return bool(o[0, 0] == 0.0 and lse[0] == -math.inf and np.isfinite(lse[4]))
+
+
+CHECKS = [check_p1, check_p4_prefixes, check_p2, check_overflow, check_sdpa, check_two_blocks,
+          check_trailing_queries, check_empty_range]
 
 
 def _build(tmpdir, name, edits):
