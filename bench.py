@@ -39,28 +39,30 @@ PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = {
     "bf16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_bf16.hip",
     "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
+    "merge": "flashattention_online_softmax_fwd_amd/csrc/fa_merge.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def kernel_hash(dtype: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
+def kernel_hash(source: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[source]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(workload: str, dtype: str):
-    """HBM bytes per launch from committed rocprofv3 counters, or None.
+def traffic_for(workload: str, source: str):
+    """HBM bytes per launch of the kernel built from KERNEL_SOURCES[source] on this
+    workload, from committed rocprofv3 counters, or None.
 
-    None when no counters were taken for this workload, or when the kernel
-    source changed since they were (its hash is stored next to them).
+    None when no counters were taken for this workload and kernel, or when the
+    kernel source changed since they were (its hash is stored next to them).
     """
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = table.get(workload)
-    if not entry or entry.get("kernel_source_sha256") != kernel_hash(dtype):
+    entry = table.get(workload, {}).get(source)
+    if not entry or entry.get("kernel_source_sha256") != kernel_hash(source):
         return None
     return entry.get("traffic_bytes_per_launch")
 
@@ -196,6 +198,92 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
     return rec
 
 
+def run_kv_workload(name, steps, warmup):
+    """Split-KV + merge over a decode-shaped workload: one step is both launches.
+
+    Reading the K/V cache dominates, so each kernel is priced against HBM: its
+    algorithmic bytes (what it must read and write at least once) over its
+    average launch duration from HIP events on the launch stream.
+    """
+    import torch
+
+    import flashattention_online_softmax_fwd_amd as fa
+    from flashattention_online_softmax_fwd_amd import _lib
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+
+    fa.load_library()
+    w = fin.KV_WORKLOADS[name]
+    q, k, v = fin.kv_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    S = _lib.fa_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk)
+    rows = w.B * w.Hq * w.Nq
+    o_part = torch.empty((S, w.B, w.Hq, w.Nq, w.d), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((S, w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def split():
+        rc = _lib.fa_fwd_splitkv(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o_part.data_ptr(),
+                                 lse_part.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, int(w.causal),
+                                 w.softmax_scale, _lib.FA_DTYPE_BF16, S, sh)
+        assert rc == 0, _lib.fa_last_error()
+
+    def merge():
+        rc = _lib.fa_merge(o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(), lse.data_ptr(), S, w.B,
+                           w.Hq, w.Nq, w.d, _lib.FA_DTYPE_BF16, sh)
+        assert rc == 0, _lib.fa_last_error()
+
+    for _ in range(warmup):
+        split()
+        merge()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        split()
+        ev[i][1].record(stream)
+        merge()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    merge_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    part_bytes = S * rows * (w.d + 1) * 4
+    split_bytes = 2 * w.B * w.d * (w.Hq * w.Nq + 2 * w.Hkv * w.Nk) + part_bytes
+    merge_bytes = part_bytes + rows * (2 * w.d + 4)
+
+    def roof(kernel, source, nbytes, ms):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic_for(w.name, source), "kernel": kernel,
+                "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes}
+
+    return {
+        "metric": "split-KV attention (split + merge) effective HBM GB/s",
+        "value": w.algorithmic_bytes * steps / wall / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": wall * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/K/V, numpy default_rng(%d))" % w.seed,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                   "d": w.d, "causal": w.causal, "num_splits": S, "flops_per_step": w.flops,
+                   "algorithmic_bytes_per_step": w.algorithmic_bytes},
+        "tflops": w.flops * steps / wall / 1e12,
+        "roofline": roof("fa::fwd_bf16_kernel (split)", "bf16", split_bytes, split_ms),
+        "merge_roofline": roof("fa::merge_kernel", "merge", merge_bytes, merge_ms),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,7 +291,8 @@ def main(argv=None):
     # so the default warm-up is long enough (~65 ms at the default workload) to reach it.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default=None, help="one of inputs.WORKLOADS (default: the metric's)")
+    ap.add_argument("--workload", default=None,
+                    help="one of inputs.WORKLOADS or inputs.KV_WORKLOADS (default: the metric's)")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -226,9 +315,14 @@ def main(argv=None):
     if args.all:
         for name in fin.WORKLOADS:
             print(json.dumps(run_workload(name, args.steps, args.warmup, False, 0.0)), flush=True)
+        for name in fin.KV_WORKLOADS:
+            print(json.dumps(run_kv_workload(name, args.steps, args.warmup)), flush=True)
         return 0
     name = args.workload or fin.BENCH_WORKLOAD
-    rec = run_workload(name, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+    if name in fin.KV_WORKLOADS:
+        rec = run_kv_workload(name, args.steps, args.warmup)
+    else:
+        rec = run_workload(name, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
     if args.copy_calibration:
         x = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
         y = torch.empty_like(x)

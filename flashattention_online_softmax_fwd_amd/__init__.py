@@ -1,8 +1,11 @@
 """FlashAttention forward for MI355X (gfx950): exact attention, online softmax.
 
 ``forward(q, k, v, causal=False, scale=None)`` returns ``(o, lse)`` computed by
-the HIP kernels in libfa.so (C ABI in include/fa.h).  torch supplies device
-memory and the stream; every step of the attention runs in the kernels.
+the HIP kernels in libfa.so (C ABI in include/fa.h).  ``forward_splitkv`` and
+``merge`` split the keys into ranges, compute each range's partial state and
+combine them; ``attention_kv`` does both for queries that are the last Nq of Nk
+positions (e.g. decoding against a cache).  torch supplies device memory and the
+stream; every step of the attention runs in the kernels.
 
 The library is loaded on first use, and a missing build raises.
 """
@@ -15,9 +18,12 @@ import torch
 from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FA_ERR_HIP, FA_ERR_INVALID_ARG,
                    FA_ERR_UNSUPPORTED, FA_OK, LibraryNotBuilt, fa_abi_version, fa_error_string,
-                   fa_fwd, fa_fwd_tiled, fa_last_error, fa_tile_shapes)
+                   fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error, fa_merge, fa_split_chunk,
+                   fa_splitkv_num_splits, fa_tile_shapes)
 
-__all__ = ["forward", "fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
+__all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "fa_fwd", "fa_fwd_tiled",
+           "fa_fwd_splitkv", "fa_merge", "fa_split_chunk", "fa_splitkv_num_splits",
+           "fa_tile_shapes", "fa_error_string",
            "fa_last_error", "fa_abi_version", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16",
            "LibraryNotBuilt", "load_library"]
@@ -93,3 +99,104 @@ def forward(q, k, v, causal=False, scale=None, block_m=None, block_n=None, out=N
     if rc != FA_OK:
         _raise(rc)
     return out, lse
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be 4-D [B, H, N, d], got %s" % (name, tuple(t.shape)))
+        if not t.is_cuda:
+            raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    if q.dtype not in _DTYPES:
+        raise ValueError("dtype %s is not supported" % q.dtype)
+    B, Hq, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q; got %s, %s, %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+
+
+def forward_splitkv(q, k, v, num_splits, causal=False, scale=None):
+    """Partial states over num_splits key ranges.
+
+    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16 CUDA tensors; the queries are
+    the last Nq of the Nk positions (causal: key j visible to query i iff
+    j <= i + Nk - Nq).  Returns (o_part [S, B, Hq, Nq, d], lse_part [S, B, Hq, Nq]),
+    float32: each range's output over its own visible keys and m + ln l, with
+    lse = -inf (o = 0) where a range holds no visible key.  Range s covers keys
+    [s*c, (s+1)*c) with c = fa_split_chunk(Nk, num_splits).
+    """
+    lib = _lib.load()
+    _check_inputs(q, k, v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = int(num_splits)
+    o_part = torch.empty((max(S, 0), B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((max(S, 0), B, Hq, Nq), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                lse_part.data_ptr(), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                                float(scale), _DTYPES[q.dtype], S, stream)
+    if rc != FA_OK:
+        _raise(rc)
+    return o_part, lse_part
+
+
+def merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None):
+    """Merge partial states: o_part [S, B, H, N, d], lse_part [S, B, H, N] float32.
+
+    Returns (o [B, H, N, d] in out_dtype, lse [B, H, N] float32).
+    """
+    lib = _lib.load()
+    for name, t in (("o_part", o_part), ("lse_part", lse_part)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous CUDA tensor" % name)
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32" % name)
+    if o_part.dim() != 5 or lse_part.shape != o_part.shape[:-1]:
+        raise ValueError("o_part must be [S, B, H, N, d] and lse_part [S, B, H, N]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    S, B, H, N, d = o_part.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=o_part.device)
+    elif (out.shape != (B, H, N, d) or out.dtype != out_dtype or out.device != o_part.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    elif (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != o_part.device
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    with torch.cuda.device(o_part.device):
+        stream = torch.cuda.current_stream(o_part.device).cuda_stream
+        rc = lib.fa_merge(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(), lse.data_ptr(), S, B, H,
+                          N, d, _DTYPES[out_dtype], stream)
+    if rc != FA_OK:
+        _raise(rc)
+    return out, lse
+
+
+def attention_kv(q, k, v, causal=False, scale=None, num_splits=None):
+    """Attention of queries that are the last Nq of Nk positions, by split-KV + merge.
+
+    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16.  num_splits defaults to
+    fa_splitkv_num_splits for the shape.  Returns (o like q, lse [B, Hq, Nq]).
+    """
+    _check_inputs(q, k, v)
+    B, Hq, Nq, _ = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if num_splits is None:
+        num_splits = max(1, fa_splitkv_num_splits(B, Hq, Hkv, max(Nq, 1), max(Nk, 1)))
+    o_part, lse_part = forward_splitkv(q, k, v, num_splits, causal=causal, scale=scale)
+    return merge(o_part, lse_part, out_dtype=q.dtype)

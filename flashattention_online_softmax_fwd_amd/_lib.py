@@ -32,6 +32,10 @@ SIGNATURES = {
     "fa_fwd": (_I, _FWD_ARGS),
     "fa_fwd_tiled": (_I, _FWD_ARGS + [_I, _I]),
     "fa_tile_shapes": (_I, [_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), _I]),
+    "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P]),
+    "fa_merge": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_split_chunk": (_I, [_I, _I]),
+    "fa_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_error_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (_I, []),
@@ -68,6 +72,24 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream):
 def fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, block_m, block_n):
     return load().fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream,
                                block_m, block_n)
+
+
+def fa_fwd_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
+                   stream):
+    return load().fa_fwd_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+                                 num_splits, stream)
+
+
+def fa_merge(o_part, lse_part, o, lse, num_splits, B, H, N, d, dtype, stream):
+    return load().fa_merge(o_part, lse_part, o, lse, num_splits, B, H, N, d, dtype, stream)
+
+
+def fa_split_chunk(Nk, num_splits):
+    return load().fa_split_chunk(Nk, num_splits)
+
+
+def fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk):
+    return load().fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk)
 
 
 def fa_tile_shapes(dtype, d):

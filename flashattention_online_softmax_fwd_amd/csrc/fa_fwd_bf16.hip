@@ -39,6 +39,15 @@
 // tile buffers are separate arrays and the key loop is unrolled by two, so every
 // access names its buffer statically: the compiler can then see that reading
 // one buffer does not wait for the loads still landing in the other.
+//
+// Split mode (SPLIT = true) computes the same state over one contiguous range of
+// keys per workgroup and writes it normalised, o = u / l and lse = m + ln l, in
+// float: the partial state of the pages' merge (kbwen.com feed, "Two blocks";
+// spicyshark.co lesson, "From softmax to attention", two workers).  The queries
+// are then the last N of Nk positions (query i at key position i + Nk - N), a
+// row with no visible key in the range gets the empty state (o = 0, lse = -inf),
+// and because that offset is arbitrary a wave's diagonal may straddle two key
+// tiles, so causal split kernels also check the mask on tiles before the last.
 #include "fa_kernels.h"
 
 #include <float.h>
@@ -103,7 +112,7 @@ struct Int {
     static constexpr int value = V;
 };
 
-template <int D, int BM, int BN, bool CAUSAL>
+template <int D, int BM, int BN, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const FwdParams p)
 {
@@ -124,34 +133,51 @@ fwd_bf16_kernel(const FwdParams p)
     __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
     __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
-    const int N = p.N;
+    const int N = p.N;                      // query rows per head
+    const int Nk = SPLIT ? p.Nk : N;        // keys per head
+    const int off = SPLIT ? p.q_off : 0;    // query i sits at key position i + off
     const int bhc = p.B * p.Hq;
+    const int bkvc = p.B * p.Hkv;
+    // Square forward: one unit per (batch, query head).  Split kernels: one unit per
+    // (split, batch, K/V head), whose rows are those of the group's G query heads.
+    const int units = SPLIT ? p.splits * bkvc : bhc;
     const int nqt = p.n_qtiles;
     const int bid = blockIdx.x;
-    int bh, qt;
+    int u, qt;
     if (p.xcd_map) {
         // Blocks go to the 8 XCDs round-robin.  Give each XCD a contiguous run of heads
         // (so its L2 holds few K/V heads at a time), each head's tiles longest first.
         const int xcd = bid & 7;
         const int k = bid >> 3;
-        bh = xcd * (bhc >> 3) + k / nqt;
+        u = xcd * (units >> 3) + k / nqt;
         const int t = k % nqt;
         qt = CAUSAL ? nqt - 1 - t : t;
     } else {
-        bh = bid % bhc;
-        qt = CAUSAL ? nqt - 1 - bid / bhc : bid / bhc;
+        u = bid % units;
+        qt = CAUSAL ? nqt - 1 - bid / units : bid / units;
     }
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
-    const int hk = hq / p.group;
-    const bf16* __restrict__ Qh = (const bf16*)p.q + (size_t)bh * N * D;
-    const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
-    const char* Vh = (const char*)p.v + (size_t)(b * p.Hkv + hk) * N * ROWB;
+    const int split = SPLIT ? u / bkvc : 0;
+    int b, hk, bh = 0;
+    if constexpr (SPLIT) {
+        const int bkv = u - split * bkvc;
+        b = bkv / p.Hkv;
+        hk = bkv - b * p.Hkv;
+    } else {
+        bh = u;
+        b = bh / p.Hq;
+        hk = (bh - b * p.Hq) / p.group;
+    }
+    // This workgroup's keys: [k_lo, k_hi), every key of the head unless split.
+    const int k_lo = SPLIT ? split * p.chunk : 0;
+    const int k_hi = SPLIT ? min(Nk, k_lo + p.chunk) : N;
+    const char* Kh = (const char*)p.k + ((size_t)(b * p.Hkv + hk) * Nk + k_lo) * ROWB;
+    const char* Vh = (const char*)p.v + ((size_t)(b * p.Hkv + hk) * Nk + k_lo) * ROWB;
     // Buffer ranges end at the head's last key: loads past it return zeros.
+    const int range_bytes = k_hi > k_lo ? (Nk - k_lo) * ROWB : 0;
     const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, range_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, N * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, range_bytes, 0x00020000);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -161,6 +187,34 @@ fwd_bf16_kernel(const FwdParams p)
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * 32;
     const int my_q = qw0 + l32;
+    // Rows of this unit.  Square forward: row my_q of head bh.  Split kernels pack the
+    // group: row r = g*N + i is query i of head hk*G + g, so one K/V tile serves every
+    // query head that reads it (one query of each when decoding).  A row's result does
+    // not depend on which rows share its tile.
+    const int R = SPLIT ? p.group * N : N;           // rows of the unit
+    const bool row_ok = my_q < R;
+    int my_pos = my_q;                               // the row's query index i
+    size_t qrow = (size_t)bh * N + my_q;             // flat [B][Hq][N] query row
+    if constexpr (SPLIT) {
+        const int g = my_q / N;
+        my_pos = my_q - g * N;
+        qrow = (size_t)(b * p.Hq + hk * p.group + g) * N + my_pos;
+    }
+    // Query indices the wave's (and the workgroup's) rows span: causal skipping uses the
+    // largest, mask checks the smallest.
+    auto pos_span = [&](int r_first, int r_last, int& pmin, int& pmax) {
+        if (!SPLIT || r_first / N == r_last / N) {
+            pmin = SPLIT ? r_first % N : r_first;
+            pmax = SPLIT ? r_last % N : r_last;
+        } else {
+            pmin = 0;
+            pmax = N - 1;
+        }
+    };
+    int w_pmin, w_pmax, g_pmin, g_pmax;
+    pos_span(qw0, SPLIT ? min(qw0 + 31, R - 1) : qw0 + 31, w_pmin, w_pmax);
+    pos_span(q0, SPLIT ? min(q0 + BM - 1, R - 1) : q0 + BM - 1, g_pmin, g_pmax);
+    (void)g_pmin;
 
     // Q as the B operand of S^T = K Q^T: dims 16kk + 8hi .. +7 of this lane's row.
     // A negative scale is folded into Q's sign so that c > 0 below; a zero scale
@@ -171,7 +225,7 @@ fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (my_q < N) raw = *(const u32x4*)(Qh + (size_t)my_q * D + 16 * kk + 8 * hi);
+        if (row_ok) raw = *(const u32x4*)((const bf16*)p.q + qrow * D + 16 * kk + 8 * hi);
         raw ^= qflip;
         qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
@@ -206,8 +260,23 @@ fwd_bf16_kernel(const FwdParams p)
     float m_ref = -INFINITY;   // exp reference, log2 units of the scaled score
     float l_run = 0.f;         // sum of P over this lane half's keys, against m_ref
 
-    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kv_end + BN - 1) / BN;
+    // Tiles of BN keys from k_lo; causal workgroups stop at their last row's diagonal.
+    const int kv_end = CAUSAL ? min(k_hi, g_pmax + 1 + off) : k_hi;
+    const int ntiles = kv_end > k_lo ? (kv_end - k_lo + BN - 1) / BN : 0;
+    if constexpr (SPLIT) {
+        if (ntiles == 0) {   // no row of this workgroup sees a key of this split: empty states
+            if (row_ok) {
+                float* Orow = (float*)p.o + ((size_t)split * bhc * N + qrow) * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(float4*)(Orow + 32 * dt + 8 * g + 4 * hi) = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (hi == 0) p.lse[(size_t)split * bhc * N + qrow] = -INFINITY;
+            }
+            return;
+        }
+    }
 
     // Tile j of K (or V) into buffer BUF, straight from HBM into LDS.
     auto issue_k = [&](int j, auto bufsel) {
@@ -252,7 +321,7 @@ fwd_bf16_kernel(const FwdParams p)
 
     // -inf for keys this lane's row may not see (only ever needed on a wave's last tile).
     auto mask_tile = [&](f32x16 (&s)[ST], int j) {
-        const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (j * BN + 4 * hi);   // relative last key
+        const int lim = (CAUSAL ? min(my_pos + off, Nk - 1) : Nk - 1) - (k_lo + j * BN + 4 * hi);   // relative last key
 #pragma unroll
         for (int t = 0; t < ST; ++t)
 #pragma unroll
@@ -328,7 +397,14 @@ fwd_bf16_kernel(const FwdParams p)
     // and V_j and loads K_{j+2} and V_{j+1}, so K runs one tile ahead of V.  A wave's only
     // masked tile is its last one (the tile holding its diagonal, or the N tail), so the
     // steady-state iteration carries no mask code.
-    const int my_last = CAUSAL ? min(ntiles - 1, (qw0 + 31) / BN) : ntiles - 1;
+    // The wave's last tile: the one holding its last row's diagonal (causal), else the
+    // last; -1 when the wave has no row below N or no visible key in this range.
+    int my_last = ntiles - 1;
+    if (CAUSAL) {
+        const int last_key = w_pmax + off;
+        my_last = last_key < k_lo ? -1 : min(ntiles - 1, (last_key - k_lo) / BN);
+    }
+    if (qw0 >= R) my_last = -1;
     // Scores of tile j live in sa for even j and in sb for odd j: no copies between tiles.
     f32x16 sa[ST], sb[ST];
 
@@ -343,9 +419,12 @@ fwd_bf16_kernel(const FwdParams p)
         bool any;
         if (j < my_last) {
             s_tile(s_nxt, Int<1 - P>{});
+            if constexpr (SPLIT && CAUSAL) {   // the diagonal may straddle this tile and the next
+                if (k_lo + j * BN + BN - 1 > w_pmin + off) mask_tile(s_cur, j);
+            }
             any = softmax(s_cur, pb, alpha);
         } else {
-            if ((CAUSAL && j * BN + BN - 1 > qw0) || (j * BN + BN > N)) mask_tile(s_cur, j);
+            if ((CAUSAL && k_lo + j * BN + BN - 1 > w_pmin + off) || (k_lo + j * BN + BN > Nk)) mask_tile(s_cur, j);
             any = softmax(s_cur, pb, alpha);
         }
         if (any) rescale_o(alpha);
@@ -364,6 +443,23 @@ fwd_bf16_kernel(const FwdParams p)
 
     // epilogue: O = u / l, LSE = m + ln l
     const float l_tot = lane_half_sum(l_run);
+    if constexpr (SPLIT) {
+        if (row_ok) {   // float partial state; l = 0 marks a row with no visible key here
+            const bool empty = !(l_tot > 0.f);
+            const float inv = empty ? 0.f : 1.f / l_tot;
+            float* Orow = (float*)p.o + ((size_t)split * bhc * N + qrow) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(float4*)(Orow + 32 * dt + 8 * g + 4 * hi) =
+                        make_float4(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                                    o[dt][4 * g + 3] * inv);
+            if (hi == 0)
+                p.lse[(size_t)split * bhc * N + qrow] = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        }
+        return;
+    }
     if (my_q < N) {
         const float inv = 1.f / l_tot;
         bf16* Orow = (bf16*)p.o + (size_t)bh * N * D + (size_t)my_q * D;
@@ -382,43 +478,55 @@ fwd_bf16_kernel(const FwdParams p)
 
 // Explicit instantiations: both the host and the device pass must see every
 // kernel the dispatch table names.
-#define FA_BF16_INSTANTIATE(D, BM, BN)                                              \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, false>(const FwdParams);  \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, true>(const FwdParams);
+#define FA_BF16_INSTANTIATE(D, BM, BN)                                                     \
+    template __global__ void fwd_bf16_kernel<D, BM, BN, false, false>(const FwdParams);  \
+    template __global__ void fwd_bf16_kernel<D, BM, BN, true, false>(const FwdParams);
+#define FA_BF16_SPLIT_INSTANTIATE(D, BM, BN)                                              \
+    template __global__ void fwd_bf16_kernel<D, BM, BN, false, true>(const FwdParams);  \
+    template __global__ void fwd_bf16_kernel<D, BM, BN, true, true>(const FwdParams);
 FA_BF16_INSTANTIATE(128, 128, 64)
 FA_BF16_INSTANTIATE(128, 128, 32)
 FA_BF16_INSTANTIATE(64, 128, 64)
 FA_BF16_INSTANTIATE(64, 128, 32)
+FA_BF16_SPLIT_INSTANTIATE(128, 128, 64)
+FA_BF16_SPLIT_INSTANTIATE(64, 128, 64)
 
 namespace {
 
-template <int D, int BM, int BN, bool CAUSAL>
+template <int D, int BM, int BN, bool CAUSAL, bool SPLIT>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
 {
-    const long long grid = (long long)p.B * p.Hq * p.n_qtiles;
+    const long long units = SPLIT ? (long long)p.splits * p.B * p.Hkv : (long long)p.B * p.Hq;
+    const long long grid = units * p.n_qtiles;
     FwdParams args = p;
-    args.xcd_map = ((p.B * p.Hq) % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
+    args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, BM, BN, CAUSAL>, dim3((unsigned)grid),
+    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, BM, BN, CAUSAL, SPLIT>, dim3((unsigned)grid),
                            dim3(BM * 2), kargs, 0, stream);
 }
 
 }  // namespace
 
-// The dispatch table is host data: it is not emitted in the device pass.
+// The dispatch tables are host data: they are not emitted in the device pass.
 #if !defined(__HIP_DEVICE_COMPILE__)
-#define FA_BF16_ENTRY(D, BM, BN)                                   \
-    {1, D, BM, BN, 0, &launch_bf16<D, BM, BN, false>},            \
-    {1, D, BM, BN, 1, &launch_bf16<D, BM, BN, true>}
+#define FA_BF16_ENTRY(D, BM, BN, SPLIT)                                   \
+    {1, D, BM, BN, 0, &launch_bf16<D, BM, BN, false, SPLIT>},            \
+    {1, D, BM, BN, 1, &launch_bf16<D, BM, BN, true, SPLIT>}
 
 // The first shape listed for each head dimension is the default.
 const KernelEntry kBf16Kernels[] = {
-    FA_BF16_ENTRY(128, 128, 64),
-    FA_BF16_ENTRY(128, 128, 32),
-    FA_BF16_ENTRY(64, 128, 64),
-    FA_BF16_ENTRY(64, 128, 32),
+    FA_BF16_ENTRY(128, 128, 64, false),
+    FA_BF16_ENTRY(128, 128, 32, false),
+    FA_BF16_ENTRY(64, 128, 64, false),
+    FA_BF16_ENTRY(64, 128, 32, false),
 };
 const int kNumBf16Kernels = sizeof(kBf16Kernels) / sizeof(kBf16Kernels[0]);
+
+const KernelEntry kBf16SplitKernels[] = {
+    FA_BF16_ENTRY(128, 128, 64, true),
+    FA_BF16_ENTRY(64, 128, 64, true),
+};
+const int kNumBf16SplitKernels = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
 
 #endif
 

@@ -18,6 +18,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
+constexpr int kMaxSplits = 1024;
+
 int fail(int code, const std::string& msg)
 {
     g_last_error = msg;
@@ -78,6 +80,9 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const uint64_t kvbytes = kvrows * (uint64_t)d * esize;
     const uint64_t lbytes = qrows * 4;
     if (qbytes >> 62 || kvbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
+    // K/V tiles are read through buffer descriptors whose range is 32-bit
+    if ((uint64_t)N * (uint64_t)d * esize > 0x7fffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "one head of K or V exceeds 2 GiB");
     if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) ||
         overlaps(o, qbytes, v, kvbytes) || overlaps(lse, lbytes, q, qbytes) ||
         overlaps(lse, lbytes, k, kvbytes) || overlaps(lse, lbytes, v, kvbytes) ||
@@ -104,11 +109,142 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.N = N;
+    p.Nk = N;
+    p.q_off = 0;
+    p.chunk = N;
+    p.splits = 1;
     p.group = Hq / Hkv;
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)folded;
     p.xcd_map = 0;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    return FA_OK;
+}
+
+// Keys per split: ceil(Nk / splits) rounded up to the 64-key tile.
+int split_chunk(int Nk, int splits)
+{
+    const int64_t per = ((int64_t)Nk + splits - 1) / splits;
+    return (int)((per + 63) / 64 * 64);
+}
+
+int run_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                int num_splits, void* stream)
+{
+    g_last_error.clear();
+    if (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_F16)
+        return fail(FA_ERR_UNSUPPORTED, "split-KV is built for bf16 inputs only");
+    if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (B < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARG, "B, Nq and Nk must be >= 0");
+    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxSplits));
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    const double folded = (double)scale * 1.4426950408889634;   // scale * log2(e)
+    if (!std::isfinite((float)folded))
+        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
+    if (B == 0 || Nq == 0) return FA_OK;                        // no query row: nothing to do
+    if (Nk == 0) return fail(FA_ERR_INVALID_ARG, "Nk must be >= 1 when there are query rows");
+    if (causal && Nq > Nk)
+        return fail(FA_ERR_INVALID_ARG, "causal needs Nq <= Nk (the queries are the last Nq positions)");
+
+    if (!q || !k || !v || !o_part || !lse_part) return fail(FA_ERR_INVALID_ARG, "null pointer");
+    const void* ptrs[5] = {q, k, v, o_part, lse_part};
+    for (const void* ptr : ptrs)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const uint64_t qrows = (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq;
+    const uint64_t qbytes = qrows * (uint64_t)d * 2;
+    const uint64_t kvbytes = (uint64_t)B * (uint64_t)Hkv * (uint64_t)Nk * (uint64_t)d * 2;
+    const uint64_t obytes = (uint64_t)num_splits * qrows * (uint64_t)d * 4;
+    const uint64_t lbytes = (uint64_t)num_splits * qrows * 4;
+    if (qbytes >> 62 || kvbytes >> 62 || obytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
+    if ((uint64_t)Nk * (uint64_t)d * 2 > 0x7fffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "one head of K or V exceeds 2 GiB");
+    if (overlaps(o_part, obytes, q, qbytes) || overlaps(o_part, obytes, k, kvbytes) ||
+        overlaps(o_part, obytes, v, kvbytes) || overlaps(lse_part, lbytes, q, qbytes) ||
+        overlaps(lse_part, lbytes, k, kvbytes) || overlaps(lse_part, lbytes, v, kvbytes) ||
+        overlaps(o_part, obytes, lse_part, lbytes))
+        return fail(FA_ERR_INVALID_ARG, "o_part and lse_part must not overlap the inputs or each other");
+
+    const fa::KernelEntry* e = nullptr;
+    for (int i = 0; i < fa::kNumBf16SplitKernels; ++i)
+        if (fa::kBf16SplitKernels[i].d == d && fa::kBf16SplitKernels[i].causal == causal)
+            e = &fa::kBf16SplitKernels[i];
+    if (!e) return fail(FA_ERR_UNSUPPORTED, "no split-KV kernel for this d");
+    // the G query heads of a K/V head share its workgroups: G*Nq packed rows per K/V head
+    const uint64_t ntiles = ((uint64_t)(Hq / Hkv) * (uint64_t)Nq + e->block_m - 1) / e->block_m;
+    const uint64_t grid = (uint64_t)num_splits * (uint64_t)B * (uint64_t)Hkv * ntiles;
+    if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+
+    fa::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o_part;
+    p.lse = lse_part;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = Nq;
+    p.Nk = Nk;
+    p.q_off = Nk - Nq;
+    p.chunk = split_chunk(Nk, num_splits);
+    p.splits = num_splits;
+    p.group = Hq / Hkv;
+    p.n_qtiles = (int)ntiles;
+    p.scale_log2 = (float)folded;
+    p.xcd_map = 0;
+    const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    return FA_OK;
+}
+
+int run_merge(const float* o_part, const float* lse_part, void* o, float* lse, int num_splits, int B,
+              int H, int N, int d, int dtype, void* stream)
+{
+    g_last_error.clear();
+    if (dtype == FA_DTYPE_F16) return fail(FA_ERR_UNSUPPORTED, "fp16 output is not built");
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
+    if (H < 1) return fail(FA_ERR_INVALID_ARG, "H must be >= 1");
+    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxSplits));
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
+    if (B == 0 || N == 0) return FA_OK;
+    if (!o_part || !lse_part || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null pointer");
+    const void* ptrs[4] = {o_part, lse_part, o, lse};
+    for (const void* ptr : ptrs)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t pbytes = (uint64_t)num_splits * rows * (uint64_t)d * 4;
+    const uint64_t plbytes = (uint64_t)num_splits * rows * 4;
+    const uint64_t obytes = rows * (uint64_t)d * (dtype == FA_DTYPE_F32 ? 4 : 2);
+    const uint64_t lbytes = rows * 4;
+    if (pbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
+    if (overlaps(o, obytes, o_part, pbytes) || overlaps(o, obytes, lse_part, plbytes) ||
+        overlaps(lse, lbytes, o_part, pbytes) || overlaps(lse, lbytes, lse_part, plbytes) ||
+        overlaps(o, obytes, lse, lbytes))
+        return fail(FA_ERR_INVALID_ARG, "o and lse must not overlap the partial states or each other");
+    if ((rows + 3) / 4 > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+
+    fa::MergeParams p;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.o = o;
+    p.lse = lse;
+    p.rows = (long long)rows;
+    p.splits = num_splits;
+    const hipError_t err = fa::launch_merge(p, d, dtype, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;
 }
@@ -132,6 +268,40 @@ int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* ls
         return FA_ERR_INVALID_ARG;
     }
     return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, block_m, block_n);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                   int num_splits, void* stream)
+{
+    return run_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
+                       stream);
+}
+
+int fa_merge(const float* o_part, const float* lse_part, void* o, float* lse, int num_splits, int B, int H,
+             int N, int d, int dtype, void* stream)
+{
+    return run_merge(o_part, lse_part, o, lse, num_splits, B, H, N, d, dtype, stream);
+}
+
+int fa_split_chunk(int Nk, int num_splits)
+{
+    if (Nk < 0 || num_splits < 1 || num_splits > kMaxSplits) return -1;
+    return split_chunk(Nk, num_splits);
+}
+
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Nq < 1 || Nk < 1) return -1;
+    // Enough workgroups to fill the chip twice over (256 CUs, two workgroups each),
+    // but at least four 64-key tiles per split.  A workgroup holds 128 rows of the
+    // G = Hq/Hkv query heads that share one K/V head.
+    const int64_t base = (int64_t)B * Hkv * (((int64_t)(Hq / Hkv) * Nq + 127) / 128);
+    int64_t s = (1024 + base - 1) / base;
+    const int64_t cap = ((int64_t)Nk + 255) / 256;
+    if (s > cap) s = cap;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
 }
 
 int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap)
@@ -170,7 +340,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 1;
+    return 2;
 }
 
 }  // extern "C"

@@ -11,9 +11,13 @@ struct FwdParams {
     const void* q;
     const void* k;
     const void* v;
-    void* o;
-    float* lse;
-    int B, Hq, Hkv, N;
+    void* o;           // [B][Hq][N][d] in the input dtype; split kernels: float [splits][B][Hq][N][d]
+    float* lse;        // [B][Hq][N]; split kernels: [splits][B][Hq][N]
+    int B, Hq, Hkv, N; // N: query rows per head
+    int Nk;            // keys per head (== N for the square forward)
+    int q_off;         // Nk - N: query i sits at key position i + q_off (causal offset)
+    int chunk;         // keys per split, a multiple of 64 (split kernels)
+    int splits;        // number of key splits (1 for the square forward)
     int group;       // Hq / Hkv: query heads per K/V head
     int n_qtiles;    // ceil(N / block_m)
     float scale_log2;  // scale * log2(e): scores go straight to the exp2 domain
@@ -37,5 +41,19 @@ extern const KernelEntry kBf16Kernels[];
 extern const int kNumBf16Kernels;
 extern const KernelEntry kF32Kernels[];
 extern const int kNumF32Kernels;
+// Split-KV partial-state kernels (bf16 inputs, float partial outputs).
+extern const KernelEntry kBf16SplitKernels[];
+extern const int kNumBf16SplitKernels;
+
+// Merge of partial states: o_part [splits][rows][d], lse_part [splits][rows] (float).
+struct MergeParams {
+    const float* o_part;
+    const float* lse_part;
+    void* o;           // [rows][d], float or bf16
+    float* lse;        // [rows]
+    long long rows;
+    int splits;
+};
+hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream);
 
 }  // namespace fa

@@ -74,6 +74,57 @@ WORKLOADS = {
 BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
 
 
+@dataclasses.dataclass(frozen=True)
+class KVWorkload:
+    """Queries that are the last Nq of Nk positions (split-KV + merge)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int = 0
+    dtype: str = "bf16"
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the mask keeps, per head."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq
+        return sum(i + off + 1 for i in range(self.Nq))
+
+    @property
+    def flops(self) -> float:
+        """4*d flops per visible (query, key) pair."""
+        return 4.0 * self.B * self.Hq * self.visible_pairs * self.d
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O (bf16) and LSE written once."""
+        return (2 * self.B * self.d * (2 * self.Hq * self.Nq + 2 * self.Hkv * self.Nk)
+                + 4 * self.B * self.Hq * self.Nq)
+
+
+# Decoding against a long cache (one new query, or a block of 16 draft queries), GQA 32/8.
+KV_WORKLOADS = {
+    "d1_bf16_decode_b8_hq32_hkv8_nk32768_d128": KVWorkload(
+        "d1_bf16_decode_b8_hq32_hkv8_nk32768_d128", 8, 32, 8, 1, 32768, 128, True, seed=1101),
+    "d2_bf16_nq16_b8_hq32_hkv8_nk32768_d128": KVWorkload(
+        "d2_bf16_nq16_b8_hq32_hkv8_nk32768_d128", 8, 32, 8, 16, 32768, 128, True, seed=1102),
+}
+
+
+def kv_workload_inputs(w: KVWorkload):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.d, w.dtype, w.seed, 1.0, Nk=w.Nk)
+
+
 def torch_dtype(dtype: str):
     if dtype == "f32":
         return torch.float32
@@ -82,12 +133,16 @@ def torch_dtype(dtype: str):
     raise ValueError("unknown dtype %r" % (dtype,))
 
 
-def make_qkv(B, Hq, Hkv, N, d, dtype="bf16", seed=0, q_mult=1.0):
-    """Seeded Q, K, V as CPU torch tensors in the input dtype."""
+def make_qkv(B, Hq, Hkv, N, d, dtype="bf16", seed=0, q_mult=1.0, Nk=None):
+    """Seeded Q, K, V as CPU torch tensors in the input dtype.
+
+    Q has N rows per head; K and V have Nk rows per head (default N).
+    """
+    nk = N if Nk is None else Nk
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
-    k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
-    v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, nk, d), dtype=np.float32)
     if q_mult != 1.0:
         q *= np.float32(q_mult)
     td = torch_dtype(dtype)

@@ -110,13 +110,71 @@ int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* ls
  */
 int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap);
 
+/*
+ * fa_fwd_splitkv: partial attention states over contiguous key ranges
+ * (split-KV).  Each range yields the state (m, l, acc) the pages carry from
+ * one block of keys, in normalised form; fa_merge then combines the ranges with
+ * the pages' merge of states of disjoint key sets (kbwen.com feed, "Two
+ * blocks": the first block alone is the answer for a query with only those keys;
+ * spicyshark.co online-softmax lesson, "From softmax to attention", two workers
+ * merging their halves, and its "Check yourself" answer).
+ *
+ *   q         [B][Hq][Nq][d] bf16; k, v [B][Hkv][Nk][d] bf16.  The queries are
+ *             the last Nq positions of the Nk keys: with causal = 1, key j is
+ *             visible to query i iff j <= i + (Nk - Nq); causal needs Nq <= Nk.
+ *             (Nq == Nk is the square problem of fa_fwd.)
+ *   splits    num_splits in 1..1024; range s holds keys
+ *             [s*c, min(Nk, (s+1)*c)) with c = fa_split_chunk(Nk, num_splits)
+ *             (ranges past Nk are empty)
+ *   o_part    [num_splits][B][Hq][Nq][d] float32 (written): the attention output
+ *             of each row over the range's visible keys alone, acc / l
+ *   lse_part  [num_splits][B][Hq][Nq] float32 (written): m + ln l of that state;
+ *             a row with no visible key in the range gets lse = -inf and o = 0
+ *             (the empty state, which carries no weight in the merge)
+ *   B, Nq     >= 0 (0: FA_OK, nothing touched); Nk >= 1 when Nq >= 1
+ *   Hq, Hkv, d, scale, stream: as for fa_fwd; dtype FA_DTYPE_BF16 (F32 and F16
+ *             return FA_ERR_UNSUPPORTED)
+ * Ownership, alignment, overlap and error rules as for fa_fwd (o_part and lse_part
+ * take the place of o and lse).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                   int dtype, int num_splits, void* stream);
+
+/*
+ * fa_merge: combine num_splits partial states per row.
+ *
+ *   o_part    [num_splits][B][H][N][d] float32, lse_part [num_splits][B][H][N]
+ *             float32: states in the form fa_fwd_splitkv writes (read only)
+ *   o         [B][H][N][d] in dtype (FA_DTYPE_F32 or FA_DTYPE_BF16), written
+ *   lse       [B][H][N] float32, written
+ *   per row:  m = max_s lse_s,  w_s = exp(lse_s - m),  lse = m + ln sum_s w_s,
+ *             o = sum_s w_s o_s / sum_s w_s; a row whose states are all empty
+ *             gets o = 0 and lse = -inf
+ *   d         64 or 128; B, N >= 0 (0: FA_OK, nothing touched); H >= 1
+ * Any set of states of disjoint key sets in this form may be merged, e.g. the
+ * outputs of fa_fwd_splitkv over different K/V shards.  Ownership, alignment,
+ * overlap and error rules as for fa_fwd.
+ */
+int fa_merge(const float* o_part, const float* lse_part, void* o, float* lse, int num_splits,
+             int B, int H, int N, int d, int dtype, void* stream);
+
+/* Keys per range of fa_fwd_splitkv: ceil(Nk / num_splits) rounded up to a
+ * multiple of 64; -1 for Nk < 0 or num_splits outside 1..1024. */
+int fa_split_chunk(int Nk, int num_splits);
+
+/* A split count that fills the GPU for this shape (about 1024 workgroups, at
+ * least 256 keys per range; a workgroup serves 128 rows of the Hq/Hkv query
+ * heads that share one K/V head), or -1 for a bad size. */
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
+
 /* Static text for a return code. */
 const char* fa_error_string(int code);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

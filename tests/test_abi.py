@@ -30,7 +30,8 @@ def declared_functions():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
-                          "fa_last_error", "fa_abi_version"}
+                          "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
+                          "fa_split_chunk", "fa_splitkv_num_splits"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -63,7 +64,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -125,3 +126,59 @@ def test_python_wrapper_checks_before_the_library():
         fa.forward(x, x, x)                     # CPU tensors are refused
     with pytest.raises(ValueError):
         fa.forward(torch.zeros(4, 64), x, x)    # wrong rank
+
+
+def call_split(lib, q=P, k=P + 0x100000, v=P + 0x200000, op=P + 0x300000, lp=P + 0x500000, B=1, Hq=2,
+               Hkv=1, Nq=4, Nk=300, d=64, causal=1, scale=0.125, dtype=1, splits=3, stream=None):
+    return lib.fa_fwd_splitkv(q, k, v, op, lp, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, splits, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(op=0), 1), (dict(lp=P + 4), 1),
+    (dict(B=-1), 1), (dict(Nq=-1), 1), (dict(Nk=-1), 1), (dict(Nk=0), 1),
+    (dict(Hq=3, Hkv=2), 1), (dict(causal=3), 1), (dict(scale=float("nan")), 1),
+    (dict(splits=0), 1), (dict(splits=1025), 1),
+    (dict(Nq=301, Nk=300), 1),                            # causal with more queries than keys
+    (dict(dtype=0), 2), (dict(dtype=2), 2), (dict(dtype=9), 1), (dict(d=96), 2),
+    (dict(op=P + 0x100000), 1),                           # o_part overlaps k
+    (dict(lp=P + 0x300010), 1),                           # lse_part overlaps o_part
+])
+def test_splitkv_rejects_bad_arguments_before_any_hip_call(lib, kw, code):
+    assert call_split(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_splitkv_and_merge_empty_problems(lib):
+    assert call_split(lib, q=0, k=0, v=0, op=0, lp=0, B=0) == 0
+    assert call_split(lib, q=0, k=0, v=0, op=0, lp=0, Nq=0) == 0
+    assert lib.fa_merge(0, 0, 0, 0, 4, 0, 2, 8, 64, 1, None) == 0
+    assert lib.fa_merge(0, 0, 0, 0, 4, 1, 2, 0, 64, 1, None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P + 0x100000, P + 0x200000, P + 0x300000, 4, 1, 2, 8, 64, 1), 1),       # null o_part
+    ((P, P + 0x100000, P + 0x200000, P + 0x300000, 0, 1, 2, 8, 64, 1), 1),       # no splits
+    ((P, P + 0x100000, P + 0x200000, P + 0x300000, 4, 1, 0, 8, 64, 1), 1),       # H = 0
+    ((P, P + 0x100000, P + 0x200000, P + 0x300000, 4, 1, 2, 8, 96, 1), 2),       # d
+    ((P, P + 0x100000, P + 0x200000, P + 0x300000, 4, 1, 2, 8, 64, 2), 2),       # fp16 output
+    ((P, P + 0x100000, P + 0x200000, P + 0x300000, 4, 1, 2, 8, 64, 7), 1),       # unknown dtype
+    ((P, P + 0x100000, P + 8, P + 0x300000, 4, 1, 2, 8, 64, 1), 1),              # o overlaps o_part
+])
+def test_merge_rejects_bad_arguments(lib, args, code):
+    assert lib.fa_merge(*args, None) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_split_chunk_and_default_splits(lib):
+    assert lib.fa_split_chunk(4096, 1) == 4096
+    assert lib.fa_split_chunk(4096, 3) == 1408          # ceil(4096/3) = 1366 -> next multiple of 64
+    assert lib.fa_split_chunk(100, 8) == 64
+    assert lib.fa_split_chunk(-1, 2) == -1 and lib.fa_split_chunk(10, 0) == -1
+    for (B, Hq, Hkv, Nq, Nk) in [(8, 32, 8, 1, 32768), (1, 8, 8, 4096, 4096), (1, 1, 1, 1, 100)]:
+        s = lib.fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk)
+        assert 1 <= s <= 1024
+        assert s <= max(1, (Nk + 255) // 256)
+    # one decode row per query head, 4 heads per K/V head: 64 workgroups before splitting
+    assert lib.fa_splitkv_num_splits(8, 32, 8, 1, 32768) == 16
+    assert lib.fa_splitkv_num_splits(0, 1, 1, 1, 1) == -1
+    assert lib.fa_splitkv_num_splits(1, 3, 2, 1, 1) == -1
