@@ -33,11 +33,12 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (and % of MFMA peak) at bf16 N=4096 d=128 causal"
 
 # MI355X published dense peaks (no sparsity): 256 CUs at 2.4 GHz.
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBPS = 8000.0
 
 KERNEL_SOURCES = {
-    "bf16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_bf16.hip",
+    "bf16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_mfma16.hip",
+    "f16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_mfma16.hip",
     "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
     "merge": "flashattention_online_softmax_fwd_amd/csrc/fa_merge.hip",
 }
@@ -186,7 +187,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
             "unit": "TFLOP/s",
             "frac": achieved / peak,
             "traffic": traffic_for(w.name, w.dtype),
-            "kernel": "fa::fwd_%s_kernel" % w.dtype,
+            "kernel": "fa::fwd_f32_kernel" if w.dtype == "f32" else "fa::fwd16_kernel<%s>" % w.dtype,
             "avg_launch_ms": avg_launch_ms,
             "min_launch_ms": min(per_ms),
             "algorithmic_flops_per_launch": w.flops,
@@ -279,7 +280,7 @@ def run_kv_workload(name, steps, warmup):
                    "d": w.d, "causal": w.causal, "num_splits": S, "flops_per_step": w.flops,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes},
         "tflops": w.flops * steps / wall / 1e12,
-        "roofline": roof("fa::fwd_bf16_kernel (split)", "bf16", split_bytes, split_ms),
+        "roofline": roof("fa::fwd16_kernel<bf16, split>", "bf16", split_bytes, split_ms),
         "merge_roofline": roof("fa::merge_kernel", "merge", merge_bytes, merge_ms),
     }
 

@@ -49,7 +49,7 @@ def _raise(rc):
 def forward(q, k, v, causal=False, scale=None, block_m=None, block_n=None, out=None, lse=None):
     """Attention forward on the GPU.
 
-    q [B, Hq, N, d]; k, v [B, Hkv, N, d]; float32 or bfloat16 CUDA tensors,
+    q [B, Hq, N, d]; k, v [B, Hkv, N, d]; float32, bfloat16 or float16 CUDA tensors,
     contiguous, on one device.  Returns (o, lse): o like q, lse [B, Hq, N]
     float32 with lse = m + ln(l) per query row.  ``scale`` defaults to
     1/sqrt(d).  ``block_m``/``block_n`` pick a compiled tile shape (see
@@ -126,7 +126,7 @@ def _check_inputs(q, k, v):
 def forward_splitkv(q, k, v, num_splits, causal=False, scale=None):
     """Partial states over num_splits key ranges.
 
-    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16 CUDA tensors; the queries are
+    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16 or float16 CUDA tensors; the queries are
     the last Nq of the Nk positions (causal: key j visible to query i iff
     j <= i + Nk - Nq).  Returns (o_part [S, B, Hq, Nq, d], lse_part [S, B, Hq, Nq]),
     float32: each range's output over its own visible keys and m + ln l, with
@@ -165,8 +165,8 @@ def merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None):
             raise ValueError("%s must be float32" % name)
     if o_part.dim() != 5 or lse_part.shape != o_part.shape[:-1]:
         raise ValueError("o_part must be [S, B, H, N, d] and lse_part [S, B, H, N]")
-    if out_dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out_dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be float32, bfloat16 or float16")
     S, B, H, N, d = o_part.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=o_part.device)
@@ -190,7 +190,7 @@ def merge(o_part, lse_part, out_dtype=torch.bfloat16, out=None, lse=None):
 def attention_kv(q, k, v, causal=False, scale=None, num_splits=None):
     """Attention of queries that are the last Nq of Nk positions, by split-KV + merge.
 
-    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16.  num_splits defaults to
+    q [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bfloat16 or float16.  num_splits defaults to
     fa_splitkv_num_splits for the shape.  Returns (o like q, lse [B, Hq, Nq]).
     """
     _check_inputs(q, k, v)

@@ -1,4 +1,5 @@
-// fa_fwd_bf16.hip -- bf16 FlashAttention forward for gfx950 (CDNA4, MI355X).
+// fa_fwd_mfma16.hip -- FlashAttention forward for gfx950 (CDNA4, MI355X) with 16-bit
+// inputs: bf16 or fp16 (the element type E), fp32 accumulation, output in E.
 //
 // One workgroup (4 waves) owns 128 query rows of one (batch, query head) and
 // walks the key tiles of its K/V head in order: query blocks outer, key blocks
@@ -7,12 +8,12 @@
 // wave's exponentials overlap the other's matrix products.
 //
 // Per key tile of BN keys, for each wave:
-//   S^T = K_tile Q_w^T          v_mfma_f32_32x32x16_bf16, fp32 accumulate
+//   S^T = K_tile Q_w^T          v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulate
 //   -inf where masked           only on tiles that cross the diagonal or the N tail
 //   mx  = rowmax S^T * c        c = scale * log2(e); one lane-half swap per row
 //   if mx > m + 8: m' = mx, a = exp2(m - m'), l *= a, O *= a      (lazy rescale)
 //   P   = exp2(S^T * c - m)     one FMA and one v_exp_f32 per score
-//   l  += rowsum P,  O^T += V_tile^T P^T        (P rounded to bf16)
+//   l  += rowsum P,  O^T += V_tile^T P^T        (P rounded to E)
 // and after the last tile O = O^T / l, LSE = (m + log2 l) * ln 2.
 //
 // This is the update the pages derive (mbrenndoerfer.com "Online Softmax
@@ -23,7 +24,7 @@
 // both measured against the same, slightly stale m, so every term carries the
 // same factor and u / l is unchanged; P stays below 2^8, far from any overflow.
 // A row whose tiles so far held no finite score keeps m = -inf and adds nothing
-// (the pages' guard for a fully masked block).  l sums the bf16-rounded P, the
+// (the pages' guard for a fully masked block).  l sums the E-rounded P, the
 // very weights the PV product uses.
 //
 // Why the scores are transposed: lane L of a 32x32 MFMA output holds one column.
@@ -55,10 +56,41 @@
 
 namespace fa {
 
-typedef __bf16 bf16;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// The element type's MFMA, pair dot product and vector types.  fp16's largest value,
+// 65504, is never approached: P stays below 2^8 (see the lazy rescale above), scores
+// and O are fp32 until the final rounding.
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+    typedef __attribute__((ext_vector_type(8))) __bf16 x8;
+    typedef __attribute__((ext_vector_type(4))) __bf16 x4;
+    typedef __attribute__((ext_vector_type(2))) __bf16 x2;
+    static __device__ __forceinline__ __attribute__((ext_vector_type(16))) float
+    mfma(x8 a, x8 b, __attribute__((ext_vector_type(16))) float c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(x2 a, x2 b, float c)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
+};
+template <>
+struct Elem<_Float16> {
+    typedef __attribute__((ext_vector_type(8))) _Float16 x8;
+    typedef __attribute__((ext_vector_type(4))) _Float16 x4;
+    typedef __attribute__((ext_vector_type(2))) _Float16 x2;
+    static __device__ __forceinline__ __attribute__((ext_vector_type(16))) float
+    mfma(x8 a, x8 b, __attribute__((ext_vector_type(16))) float c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(x2 a, x2 b, float c)
+    {
+        return __builtin_amdgcn_fdot2(a, b, c, false);
+    }
+};
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -112,10 +144,13 @@ struct Int {
     static constexpr int value = V;
 };
 
-template <int D, int BM, int BN, bool CAUSAL, bool SPLIT>
+template <typename E, int D, int BM, int BN, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_kernel(const FwdParams p)
+fwd16_kernel(const FwdParams p)
 {
+    typedef typename Elem<E>::x8 ex8;
+    typedef typename Elem<E>::x4 ex4;
+    typedef typename Elem<E>::x2 ex2;
     static_assert(BM == 128, "four waves of 32 query rows");
     static_assert(D == 64 || D == 128, "head dimension");
     static_assert(BN % 32 == 0, "key tile");
@@ -221,13 +256,13 @@ fwd_bf16_kernel(const FwdParams p)
     // becomes the smallest normal float, which leaves every exp2 argument at 0.
     const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned qflip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
-    bf16x8 qf[DK];
+    ex8 qf[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (row_ok) raw = *(const u32x4*)((const bf16*)p.q + qrow * D + 16 * kk + 8 * hi);
+        if (row_ok) raw = *(const u32x4*)((const E*)p.q + qrow * D + 16 * kk + 8 * hi);
         raw ^= qflip;
-        qf[kk] = __builtin_bit_cast(bf16x8, raw);
+        qf[kk] = __builtin_bit_cast(ex8, raw);
     }
 
     // Per-lane LDS byte offsets of the K operand: row 32t + l32, logical chunk 2kk + hi.
@@ -313,8 +348,8 @@ fwd_bf16_kernel(const FwdParams p)
             for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const bf16x8 a = *(const FA_LDS bf16x8*)(kb + 32 * t * ROWB + koff[kk]);
-                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[t], 0, 0, 0);
+                const ex8 a = *(const FA_LDS ex8*)(kb + 32 * t * ROWB + koff[kk]);
+                s[t] = Elem<E>::mfma(a, qf[kk], s[t]);
             }
         }
     };
@@ -331,7 +366,7 @@ fwd_bf16_kernel(const FwdParams p)
 
     // Online-softmax update for one tile of scores: returns the rescale factor for O
     // (1 where the reference did not move) and whether any row of the wave moved.
-    auto softmax = [&](f32x16 (&s)[ST], bf16x8 (&pb)[ST][2], float& alpha) -> bool {
+    auto softmax = [&](f32x16 (&s)[ST], ex8 (&pb)[ST][2], float& alpha) -> bool {
         float mx0 = s[0][0], mx1 = s[0][1];
 #pragma unroll
         for (int t = 0; t < ST; ++t)
@@ -348,20 +383,20 @@ fwd_bf16_kernel(const FwdParams p)
         m_ref = m_new;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;   // nothing finite yet: P = 0
         float ls0 = 0.f, ls1 = 0.f;
-        const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+        const ex2 one = {(E)1.f, (E)1.f};
 #pragma unroll
         for (int t = 0; t < ST; ++t)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    bf16x2 pair;
-                    pair[0] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e], c, -m_use));
-                    pair[1] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e + 1], c, -m_use));
+                    ex2 pair;
+                    pair[0] = (E)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e], c, -m_use));
+                    pair[1] = (E)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e + 1], c, -m_use));
                     pb[t][u][e] = pair[0];
                     pb[t][u][e + 1] = pair[1];
-                    if (e & 2) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls1, false);
-                    else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls0, false);
+                    if (e & 2) ls1 = Elem<E>::dot2(pair, one, ls1);
+                    else ls0 = Elem<E>::dot2(pair, one, ls0);
                 }
         l_run = l_run * alpha + (ls0 + ls1);
         return __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -375,7 +410,7 @@ fwd_bf16_kernel(const FwdParams p)
     };
 
     // O^T += V_tile^T P^T from the V buffer BUF.
-    auto pv = [&](const bf16x8 (&pb)[ST][2], auto bufsel) {
+    auto pv = [&](const ex8 (&pb)[ST][2], auto bufsel) {
         const char* vb = decltype(bufsel)::value == 0 ? v_lds0 : v_lds1;
 #pragma unroll
         for (int t = 0; t < ST; ++t)
@@ -387,8 +422,7 @@ fwd_bf16_kernel(const FwdParams p)
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vrow + voff[0][dt]));
                     const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vrow + voff[1][dt]));
                     const i16x8 both = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[t][u],
-                                                                   o[dt], 0, 0, 0);
+                    o[dt] = Elem<E>::mfma(__builtin_bit_cast(ex8, both), pb[t][u], o[dt]);
                 }
     };
 
@@ -414,7 +448,7 @@ fwd_bf16_kernel(const FwdParams p)
         if (j + 2 < ntiles) issue_k(j + 2, Int<P>{});
         if (j + 1 < ntiles) issue_v(j + 1, Int<1 - P>{});
         if (j > my_last) return;                   // this wave's rows are done
-        bf16x8 pb[ST][2];
+        ex8 pb[ST][2];
         float alpha;
         bool any;
         if (j < my_last) {
@@ -462,46 +496,46 @@ fwd_bf16_kernel(const FwdParams p)
     }
     if (my_q < N) {
         const float inv = 1.f / l_tot;
-        bf16* Orow = (bf16*)p.o + (size_t)bh * N * D + (size_t)my_q * D;
+        E* Orow = (E*)p.o + (size_t)bh * N * D + (size_t)my_q * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                bf16x4 w;
+                ex4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dt][4 * g + e] * inv);
-                *(bf16x4*)(Orow + 32 * dt + 8 * g + 4 * hi) = w;
+                for (int e = 0; e < 4; ++e) w[e] = (E)(o[dt][4 * g + e] * inv);
+                *(ex4*)(Orow + 32 * dt + 8 * g + 4 * hi) = w;
             }
         if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
 // Explicit instantiations: both the host and the device pass must see every
-// kernel the dispatch table names.
-#define FA_BF16_INSTANTIATE(D, BM, BN)                                                     \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, false, false>(const FwdParams);  \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, true, false>(const FwdParams);
-#define FA_BF16_SPLIT_INSTANTIATE(D, BM, BN)                                              \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, false, true>(const FwdParams);  \
-    template __global__ void fwd_bf16_kernel<D, BM, BN, true, true>(const FwdParams);
-FA_BF16_INSTANTIATE(128, 128, 64)
-FA_BF16_INSTANTIATE(128, 128, 32)
-FA_BF16_INSTANTIATE(64, 128, 64)
-FA_BF16_INSTANTIATE(64, 128, 32)
-FA_BF16_SPLIT_INSTANTIATE(128, 128, 64)
-FA_BF16_SPLIT_INSTANTIATE(64, 128, 64)
+// kernel the dispatch tables name.
+#define FA16_INSTANTIATE(E, D, BM, BN, SPLIT)                                                 \
+    template __global__ void fwd16_kernel<E, D, BM, BN, false, SPLIT>(const FwdParams);   \
+    template __global__ void fwd16_kernel<E, D, BM, BN, true, SPLIT>(const FwdParams);
+#define FA16_INSTANTIATE_TYPE(E)                \
+    FA16_INSTANTIATE(E, 128, 128, 64, false)    \
+    FA16_INSTANTIATE(E, 128, 128, 32, false)    \
+    FA16_INSTANTIATE(E, 64, 128, 64, false)     \
+    FA16_INSTANTIATE(E, 64, 128, 32, false)     \
+    FA16_INSTANTIATE(E, 128, 128, 64, true)     \
+    FA16_INSTANTIATE(E, 64, 128, 64, true)
+FA16_INSTANTIATE_TYPE(__bf16)
+FA16_INSTANTIATE_TYPE(_Float16)
 
 namespace {
 
-template <int D, int BM, int BN, bool CAUSAL, bool SPLIT>
-hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
+template <typename E, int D, int BM, int BN, bool CAUSAL, bool SPLIT>
+hipError_t launch16(const FwdParams& p, hipStream_t stream)
 {
     const long long units = SPLIT ? (long long)p.splits * p.B * p.Hkv : (long long)p.B * p.Hq;
     const long long grid = units * p.n_qtiles;
     FwdParams args = p;
     args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, BM, BN, CAUSAL, SPLIT>, dim3((unsigned)grid),
+    return hipLaunchKernel((const void*)&fwd16_kernel<E, D, BM, BN, CAUSAL, SPLIT>, dim3((unsigned)grid),
                            dim3(BM * 2), kargs, 0, stream);
 }
 
@@ -509,24 +543,28 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t stream)
 
 // The dispatch tables are host data: they are not emitted in the device pass.
 #if !defined(__HIP_DEVICE_COMPILE__)
-#define FA_BF16_ENTRY(D, BM, BN, SPLIT)                                   \
-    {1, D, BM, BN, 0, &launch_bf16<D, BM, BN, false, SPLIT>},            \
-    {1, D, BM, BN, 1, &launch_bf16<D, BM, BN, true, SPLIT>}
+#define FA16_ENTRY(E, DT, D, BM, BN, SPLIT)                                   \
+    {DT, D, BM, BN, 0, &launch16<E, D, BM, BN, false, SPLIT>},               \
+    {DT, D, BM, BN, 1, &launch16<E, D, BM, BN, true, SPLIT>}
 
 // The first shape listed for each head dimension is the default.
-const KernelEntry kBf16Kernels[] = {
-    FA_BF16_ENTRY(128, 128, 64, false),
-    FA_BF16_ENTRY(128, 128, 32, false),
-    FA_BF16_ENTRY(64, 128, 64, false),
-    FA_BF16_ENTRY(64, 128, 32, false),
-};
-const int kNumBf16Kernels = sizeof(kBf16Kernels) / sizeof(kBf16Kernels[0]);
+#define FA16_TABLE(E, DT)                          \
+    FA16_ENTRY(E, DT, 128, 128, 64, false),        \
+    FA16_ENTRY(E, DT, 128, 128, 32, false),        \
+    FA16_ENTRY(E, DT, 64, 128, 64, false),         \
+    FA16_ENTRY(E, DT, 64, 128, 32, false)
+#define FA16_SPLIT_TABLE(E, DT)                    \
+    FA16_ENTRY(E, DT, 128, 128, 64, true),         \
+    FA16_ENTRY(E, DT, 64, 128, 64, true)
 
-const KernelEntry kBf16SplitKernels[] = {
-    FA_BF16_ENTRY(128, 128, 64, true),
-    FA_BF16_ENTRY(64, 128, 64, true),
-};
+const KernelEntry kBf16Kernels[] = {FA16_TABLE(__bf16, 1)};
+const int kNumBf16Kernels = sizeof(kBf16Kernels) / sizeof(kBf16Kernels[0]);
+const KernelEntry kF16Kernels[] = {FA16_TABLE(_Float16, 2)};
+const int kNumF16Kernels = sizeof(kF16Kernels) / sizeof(kF16Kernels[0]);
+const KernelEntry kBf16SplitKernels[] = {FA16_SPLIT_TABLE(__bf16, 1)};
 const int kNumBf16SplitKernels = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
+const KernelEntry kF16SplitKernels[] = {FA16_SPLIT_TABLE(_Float16, 2)};
+const int kNumF16SplitKernels = sizeof(kF16SplitKernels) / sizeof(kF16SplitKernels[0]);
 
 #endif
 

@@ -26,10 +26,26 @@ int fail(int code, const std::string& msg)
     return code;
 }
 
+bool known_dtype(int dtype)
+{
+    return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
+}
+
+// The square-forward kernels compiled for a dtype (n = 0 for an unknown one).
+const fa::KernelEntry* table_for(int dtype, int* n)
+{
+    switch (dtype) {
+    case FA_DTYPE_F32: *n = fa::kNumF32Kernels; return fa::kF32Kernels;
+    case FA_DTYPE_BF16: *n = fa::kNumBf16Kernels; return fa::kBf16Kernels;
+    case FA_DTYPE_F16: *n = fa::kNumF16Kernels; return fa::kF16Kernels;
+    default: *n = 0; return nullptr;
+    }
+}
+
 const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n)
 {
-    const fa::KernelEntry* table = dtype == FA_DTYPE_BF16 ? fa::kBf16Kernels : fa::kF32Kernels;
-    const int n = dtype == FA_DTYPE_BF16 ? fa::kNumBf16Kernels : fa::kNumF32Kernels;
+    int n = 0;
+    const fa::KernelEntry* table = table_for(dtype, &n);
     for (int i = 0; i < n; ++i) {
         const fa::KernelEntry& e = table[i];
         if (e.d != d || e.causal != causal) continue;
@@ -50,9 +66,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
         int N, int d, int causal, float scale, int dtype, void* stream, int block_m, int block_n)
 {
     g_last_error.clear();
-    if (dtype == FA_DTYPE_F16) return fail(FA_ERR_UNSUPPORTED, "fp16 inputs are not built");
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
     if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
     if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
     if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
@@ -134,9 +148,8 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
                 int num_splits, void* stream)
 {
     g_last_error.clear();
-    if (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_F16)
-        return fail(FA_ERR_UNSUPPORTED, "split-KV is built for bf16 inputs only");
-    if (dtype != FA_DTYPE_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "split-KV is built for 16-bit inputs only");
     if (B < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARG, "B, Nq and Nk must be >= 0");
     if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
     if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
@@ -173,10 +186,11 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
         overlaps(o_part, obytes, lse_part, lbytes))
         return fail(FA_ERR_INVALID_ARG, "o_part and lse_part must not overlap the inputs or each other");
 
+    const fa::KernelEntry* split_table = dtype == FA_DTYPE_BF16 ? fa::kBf16SplitKernels : fa::kF16SplitKernels;
+    const int split_n = dtype == FA_DTYPE_BF16 ? fa::kNumBf16SplitKernels : fa::kNumF16SplitKernels;
     const fa::KernelEntry* e = nullptr;
-    for (int i = 0; i < fa::kNumBf16SplitKernels; ++i)
-        if (fa::kBf16SplitKernels[i].d == d && fa::kBf16SplitKernels[i].causal == causal)
-            e = &fa::kBf16SplitKernels[i];
+    for (int i = 0; i < split_n && !e; ++i)
+        if (split_table[i].d == d && split_table[i].causal == causal) e = &split_table[i];
     if (!e) return fail(FA_ERR_UNSUPPORTED, "no split-KV kernel for this d");
     // the G query heads of a K/V head share its workgroups: G*Nq packed rows per K/V head
     const uint64_t ntiles = ((uint64_t)(Hq / Hkv) * (uint64_t)Nq + e->block_m - 1) / e->block_m;
@@ -210,9 +224,7 @@ int run_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
               int H, int N, int d, int dtype, void* stream)
 {
     g_last_error.clear();
-    if (dtype == FA_DTYPE_F16) return fail(FA_ERR_UNSUPPORTED, "fp16 output is not built");
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
     if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
     if (H < 1) return fail(FA_ERR_INVALID_ARG, "H must be >= 1");
     if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
@@ -306,10 +318,10 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk)
 
 int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap)
 {
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return -1;
+    if (!known_dtype(dtype)) return -1;
     if (d != 64 && d != 128) return -1;
-    const fa::KernelEntry* table = dtype == FA_DTYPE_BF16 ? fa::kBf16Kernels : fa::kF32Kernels;
-    const int n = dtype == FA_DTYPE_BF16 ? fa::kNumBf16Kernels : fa::kNumF32Kernels;
+    int n = 0;
+    const fa::KernelEntry* table = table_for(dtype, &n);
     int count = 0;
     for (int i = 0; i < n; ++i) {
         if (table[i].d != d || table[i].causal != 0) continue;

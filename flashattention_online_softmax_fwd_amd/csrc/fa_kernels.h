@@ -39,21 +39,25 @@ struct KernelEntry {
 // Tables defined by the kernel translation units.
 extern const KernelEntry kBf16Kernels[];
 extern const int kNumBf16Kernels;
+extern const KernelEntry kF16Kernels[];
+extern const int kNumF16Kernels;
 extern const KernelEntry kF32Kernels[];
 extern const int kNumF32Kernels;
-// Split-KV partial-state kernels (bf16 inputs, float partial outputs).
+// Split-KV partial-state kernels (16-bit inputs, float partial outputs).
 extern const KernelEntry kBf16SplitKernels[];
 extern const int kNumBf16SplitKernels;
+extern const KernelEntry kF16SplitKernels[];
+extern const int kNumF16SplitKernels;
 
 // Merge of partial states: o_part [splits][rows][d], lse_part [splits][rows] (float).
 struct MergeParams {
     const float* o_part;
     const float* lse_part;
-    void* o;           // [rows][d], float or bf16
+    void* o;           // [rows][d], float, bf16 or fp16
     float* lse;        // [rows]
     long long rows;
     int splits;
 };
-hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream);   // FA_DTYPE_*
 
 }  // namespace fa

@@ -24,7 +24,7 @@
 
 namespace fa {
 
-template <int D, bool BF16_OUT>
+template <int D, typename OutT>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeParams p)
 {
     constexpr int PER = D / 64;            // floats per lane
@@ -81,32 +81,37 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeParams p)
     }
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
-    if constexpr (BF16_OUT) {
-        __bf16* dst = (__bf16*)p.o + row * D + PER * lane;
+    OutT* dst = (OutT*)p.o + row * D + PER * lane;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) dst[e] = (__bf16)(acc[e] * inv);
-    } else {
-        float* dst = (float*)p.o + row * D + PER * lane;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) dst[e] = acc[e] * inv;
-    }
+    for (int e = 0; e < PER; ++e) dst[e] = (OutT)(acc[e] * inv);   // round to nearest even
     if (lane == 0) p.lse[row] = empty ? -INFINITY : m + logf(l);
 }
 
-template __global__ void merge_kernel<128, false>(const MergeParams);
-template __global__ void merge_kernel<128, true>(const MergeParams);
-template __global__ void merge_kernel<64, false>(const MergeParams);
-template __global__ void merge_kernel<64, true>(const MergeParams);
+template __global__ void merge_kernel<128, float>(const MergeParams);
+template __global__ void merge_kernel<128, __bf16>(const MergeParams);
+template __global__ void merge_kernel<128, _Float16>(const MergeParams);
+template __global__ void merge_kernel<64, float>(const MergeParams);
+template __global__ void merge_kernel<64, __bf16>(const MergeParams);
+template __global__ void merge_kernel<64, _Float16>(const MergeParams);
 
 #if !defined(__HIP_DEVICE_COMPILE__)
+namespace {
+template <int D>
+const void* merge_fn(int out_dtype)
+{
+    // out_dtype: 0 float32, 1 bfloat16, 2 float16 (validated by the caller)
+    if (out_dtype == 1) return (const void*)&merge_kernel<D, __bf16>;
+    if (out_dtype == 2) return (const void*)&merge_kernel<D, _Float16>;
+    return (const void*)&merge_kernel<D, float>;
+}
+}  // namespace
+
 hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream)
 {
     const long long grid = (p.rows + 3) / 4;
     MergeParams args = p;
     void* kargs[] = {&args};
-    const bool bf = out_dtype == 1;
-    const void* fn = d == 128 ? (bf ? (const void*)&merge_kernel<128, true> : (const void*)&merge_kernel<128, false>)
-                              : (bf ? (const void*)&merge_kernel<64, true> : (const void*)&merge_kernel<64, false>);
+    const void* fn = d == 128 ? merge_fn<128>(out_dtype) : merge_fn<64>(out_dtype);
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), kargs, 0, stream);
 }
 #endif

@@ -8,7 +8,7 @@ share.
 Recipe: ``numpy.random.default_rng(seed)`` draws Q, K and V (in that order) as
 float32 standard normals of shape [B, Hq, N, d], [B, Hkv, N, d], [B, Hkv, N, d];
 Q is then multiplied by ``q_mult``; bf16 workloads round to bfloat16 with
-round-to-nearest-even (``torch.Tensor.to``).  The oracle reads the rounded
+round-to-nearest-even (``torch.Tensor.to``), fp16 ones likewise.  The oracle reads the rounded
 values upcast exactly to float64.
 """
 from __future__ import annotations
@@ -28,7 +28,7 @@ class Workload:
     Hkv: int
     N: int
     d: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     causal: bool
     q_mult: float = 1.0
     scale: float | None = None   # None: 1/sqrt(d)
@@ -69,6 +69,10 @@ WORKLOADS = {
     "c5s_bf16_n4096_d128_causal_q12_scale1": Workload("c5s_bf16_n4096_d128_causal_q12_scale1", 1, 8, 8,
                                                       4096, 128, "bf16", True, q_mult=12.0, scale=1.0,
                                                       seed=1006),
+    # fp16 inputs at the shapes of the d = 64 and the bench workload
+    "c2h_f16_n2048_d64": Workload("c2h_f16_n2048_d64", 4, 16, 16, 2048, 64, "f16", False, seed=1007),
+    "c3h_f16_n4096_d128_causal": Workload("c3h_f16_n4096_d128_causal", 2, 32, 32, 4096, 128, "f16", True,
+                                          seed=1008),
 }
 
 BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
@@ -130,6 +134,8 @@ def torch_dtype(dtype: str):
         return torch.float32
     if dtype == "bf16":
         return torch.bfloat16
+    if dtype == "f16":
+        return torch.float16
     raise ValueError("unknown dtype %r" % (dtype,))
 
 

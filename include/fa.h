@@ -59,7 +59,7 @@ extern "C" {
 typedef enum fa_dtype {
     FA_DTYPE_F32 = 0,   /* float32 inputs, float32 MFMA, float32 output      */
     FA_DTYPE_BF16 = 1,  /* bfloat16 inputs, fp32 accumulate, bfloat16 output  */
-    FA_DTYPE_F16 = 2    /* reserved: returns FA_ERR_UNSUPPORTED               */
+    FA_DTYPE_F16 = 2    /* float16 inputs, fp32 accumulate, float16 output    */
 } fa_dtype;
 
 enum {
@@ -82,7 +82,7 @@ enum {
  *   causal    0 or 1
  *   scale     any finite float; multiplies q.k before the softmax
  *             (1/sqrt(d) gives the usual attention)
- *   dtype     FA_DTYPE_F32 or FA_DTYPE_BF16
+ *   dtype     FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16
  *   stream    hipStream_t to enqueue on; NULL means the default stream
  *
  * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
@@ -119,7 +119,7 @@ int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap);
  * spicyshark.co online-softmax lesson, "From softmax to attention", two workers
  * merging their halves, and its "Check yourself" answer).
  *
- *   q         [B][Hq][Nq][d] bf16; k, v [B][Hkv][Nk][d] bf16.  The queries are
+ *   q         [B][Hq][Nq][d]; k, v [B][Hkv][Nk][d]; bf16 or fp16.  The queries are
  *             the last Nq positions of the Nk keys: with causal = 1, key j is
  *             visible to query i iff j <= i + (Nk - Nq); causal needs Nq <= Nk.
  *             (Nq == Nk is the square problem of fa_fwd.)
@@ -132,8 +132,8 @@ int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap);
  *             a row with no visible key in the range gets lse = -inf and o = 0
  *             (the empty state, which carries no weight in the merge)
  *   B, Nq     >= 0 (0: FA_OK, nothing touched); Nk >= 1 when Nq >= 1
- *   Hq, Hkv, d, scale, stream: as for fa_fwd; dtype FA_DTYPE_BF16 (F32 and F16
- *             return FA_ERR_UNSUPPORTED)
+ *   Hq, Hkv, d, scale, stream: as for fa_fwd; dtype FA_DTYPE_BF16 or
+ *             FA_DTYPE_F16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED)
  * Ownership, alignment, overlap and error rules as for fa_fwd (o_part and lse_part
  * take the place of o and lse).
  */
@@ -146,7 +146,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, f
  *
  *   o_part    [num_splits][B][H][N][d] float32, lse_part [num_splits][B][H][N]
  *             float32: states in the form fa_fwd_splitkv writes (read only)
- *   o         [B][H][N][d] in dtype (FA_DTYPE_F32 or FA_DTYPE_BF16), written
+ *   o         [B][H][N][d] in dtype (FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16), written
  *   lse       [B][H][N] float32, written
  *   per row:  m = max_s lse_s,  w_s = exp(lse_s - m),  lse = m + ln sum_s w_s,
  *             o = sum_s w_s o_s / sum_s w_s; a row whose states are all empty

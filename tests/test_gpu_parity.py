@@ -6,8 +6,10 @@ the oracle reads the very tensors the GPU reads, upcast exactly to float64.
 Tolerance (the method's bar, read elementwise in allclose form because values
 near zero make a pure relative bound meaningless and rounding O to bf16 alone
 can cost up to 1/64 where |O| is in [4, 8)):
-    bf16 inputs:  |x - r| <= 1e-2 + 2e-2 * |r|   on O and on LSE
-    fp32 inputs:  |x - r| <= 1e-5                on O and on LSE
+    bf16 inputs:  |x - r| <= 1e-2 + 2e-2 * |r|       on O and on LSE
+    fp16 inputs:  |x - r| <= 1.25e-3 + 2.5e-3 * |r|  (the bf16 bar times 2^-3, the
+                  ratio of the two formats' unit roundoffs)
+    fp32 inputs:  |x - r| <= 1e-5                    on O and on LSE
 Every O and LSE value must also be finite.
 """
 import json
@@ -46,7 +48,9 @@ def oracle():
 
 
 def tol(dtype):
-    return (1e-2, 2e-2) if dtype == "bf16" else (1e-5, 0.0)
+    """bf16: the method's bar; fp16: that bar scaled by 2^-3, the ratio of fp16's unit
+    roundoff (2^-11) to bf16's (2^-8); fp32: 1e-5."""
+    return {"bf16": (1e-2, 2e-2), "f16": (1.25e-3, 2.5e-3), "f32": (1e-5, 0.0)}[dtype]
 
 
 def check(x, r, dtype, what):
@@ -113,7 +117,7 @@ def page_bar(dtype, want, printed_places):
     return atol + rtol * abs(want) + 0.5 * 10.0 ** (-printed_places) / 64
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_p1_worked_example(fa, dtype, d):
     g = golden("p1_four_scores.json")
@@ -140,7 +144,7 @@ def test_p2_not_the_block_mean(fa):
     assert abs(o[0, 0, 0, 0].item() - g["wrong_block_mean"]) > 0.2
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_p4_tables_as_causal_prefixes(fa, dtype):
     g = golden("p4_worked_example.json")
     q, k, v = embed(g["scores"], g["values"], 64, dtype, 1 / 64)
@@ -167,7 +171,7 @@ def test_p4_tables_as_causal_prefixes(fa, dtype):
 TINY_N = [1, 2, 3, 5, 17, 63, 64, 65, 127, 128, 129, 255, 257]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", TINY_N)
@@ -175,17 +179,18 @@ def test_tiny_shapes(fa, oracle, N, d, causal, dtype):
     parity(fa, oracle, 1, 2, 1, N, d, dtype, causal, seed=N * 10 + d)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 2), (4, 2), (8, 1), (8, 8)])
 def test_head_layouts(fa, oracle, Hq, Hkv, dtype):
     parity(fa, oracle, 2, Hq, Hkv, 193, 128, dtype, True, seed=Hq * 10 + Hkv)
     parity(fa, oracle, 2, Hq, Hkv, 150, 64, dtype, False, seed=Hq * 10 + Hkv + 1)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f16", 64), ("f32", 128),
+                                     ("f32", 64)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_tile_shape(fa, oracle, dtype, d, causal):
-    code = fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32
+    code = {"bf16": fa.FA_DTYPE_BF16, "f16": fa.FA_DTYPE_F16, "f32": fa.FA_DTYPE_F32}[dtype]
     shapes = fa.fa_tile_shapes(code, d)
     assert len(shapes) >= 2
     for tile in shapes:
@@ -196,7 +201,7 @@ def test_every_tile_shape(fa, oracle, dtype, d, causal):
 
 # ------------------------------------------------------------- closed forms
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_constant_values(fa, dtype, causal):
     q, k, v = fin.make_qkv(1, 4, 4, 300, 128, dtype, 3, q_mult=12.0)
@@ -206,7 +211,7 @@ def test_constant_values(fa, dtype, causal):
     assert torch.all(torch.isfinite(lse))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_queries_average_the_visible_values(fa, dtype, causal):
     q, k, v = fin.make_qkv(1, 2, 2, 200, 64, dtype, 4)
@@ -224,7 +229,7 @@ def test_zero_queries_average_the_visible_values(fa, dtype, causal):
 
 
 def test_single_key_gives_its_value(fa):
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32", "bf16", "f16"):
         q, k, v = fin.make_qkv(2, 2, 1, 1, 128, dtype, 5)
         o, lse = run_gpu(fa, q, k, v, True, 0.3)
         assert torch.equal(o, v.float().repeat_interleave(2, dim=1))
@@ -234,7 +239,7 @@ def test_single_key_gives_its_value(fa):
 
 def test_max_in_the_last_key_tile(fa, oracle):
     """Every row's largest score is in the last key tile: all earlier sums must shrink."""
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32", "bf16", "f16"):
         q, k, v = fin.make_qkv(1, 2, 2, 517, 128, dtype, 6)
         u = q[:, :, :1].float()
         q = u.expand_as(q).to(q.dtype).contiguous()            # one query vector for every row
@@ -292,8 +297,8 @@ def test_invalid_arguments_raise(fa):
     with pytest.raises(NotImplementedError):
         x = torch.zeros(1, 1, 16, 96, device="cuda", dtype=torch.bfloat16)
         fa.forward(x, x, x)
-    with pytest.raises(NotImplementedError):
-        x = torch.zeros(1, 1, 16, 64, device="cuda", dtype=torch.float16)
+    with pytest.raises(ValueError):
+        x = torch.zeros(1, 1, 16, 64, device="cuda", dtype=torch.float64)
         fa.forward(x, x, x)
     with pytest.raises(ValueError):
         x = torch.zeros(1, 1, 16, 64, device="cuda", dtype=torch.bfloat16)

@@ -6,10 +6,11 @@ the pages' merge.  The oracle side is ``attention_kv`` (the plain definition
 over a key range) and ``merge_partials`` (the pages' merge in fp64), both pinned
 on the CPU in test_oracle_splitkv.
 
-Tolerance: the bf16 bar of the forward, |x - r| <= 1e-2 + 2e-2 |r|, on partial
-o and lse (P is rounded to bf16 before the PV product, as in the forward) and on
-the merged result; the merge kernel alone, on float32 states, is held to
-|x - r| <= 2e-6 + 2e-6 |r| for a float32 output and the bf16 bar for a bf16 one.
+Tolerance: the forward's bar for the input dtype, |x - r| <= 1e-2 + 2e-2 |r| for
+bf16 and 1.25e-3 + 2.5e-3 |r| for fp16, on partial o and lse (P is rounded to the
+input dtype before the PV product, as in the forward) and on the merged result;
+the merge kernel alone, on float32 states, is held to |x - r| <= 2e-6 + 2e-6 |r|
+for a float32 output and the 16-bit bar for a 16-bit one.
 Empty states must be exactly o = 0, lse = -inf.
 """
 import math
@@ -55,6 +56,8 @@ def check(x, r, atol, rtol, what):
 
 
 BF16 = (1e-2, 2e-2)
+F16 = (1.25e-3, 2.5e-3)
+TOL = {"bf16": BF16, "f16": F16}
 
 # B, Hq, Hkv, Nq, Nk, d, causal, splits
 SPLIT_CASES = [
@@ -71,16 +74,17 @@ SPLIT_CASES = [
 ]
 
 
-def _case_inputs(B, Hq, Hkv, Nq, Nk, d, seed):
-    return fin.make_qkv(B, Hq, Hkv, Nq, d, "bf16", seed, 1.0, Nk=Nk)
+def _case_inputs(B, Hq, Hkv, Nq, Nk, d, seed, dtype):
+    return fin.make_qkv(B, Hq, Hkv, Nq, d, dtype, seed, 1.0, Nk=Nk)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("case", SPLIT_CASES)
-def test_partial_states_match_the_oracle_range_by_range(fa, oracle, case):
+def test_partial_states_match_the_oracle_range_by_range(fa, oracle, case, dtype):
     B, Hq, Hkv, Nq, Nk, d, causal, S = case
-    q, k, v = _case_inputs(B, Hq, Hkv, Nq, Nk, d, 2000 + Nq + Nk + S)
+    q, k, v = _case_inputs(B, Hq, Hkv, Nq, Nk, d, 2000 + Nq + Nk + S, dtype)
     sc = 1.0 / math.sqrt(d)
-    print("splitkv partial states", case, flush=True)
+    print("splitkv partial states", case, dtype, flush=True)
     op, lp = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), S, causal=causal, scale=sc)
     torch.cuda.synchronize()
     op, lp = op.cpu().numpy(), lp.cpu().numpy()
@@ -89,31 +93,33 @@ def test_partial_states_match_the_oracle_range_by_range(fa, oracle, case):
         lo, hi = min(Nk, s * c), min(Nk, (s + 1) * c)
         ro, rl = oracle.attention_kv(q, k, v, causal=causal, scale=sc, k_range=(lo, hi))
         tag = "%s range %d [%d, %d)" % (case, s, lo, hi)
-        check(lp[s], rl, *BF16, "lse_part " + tag)
+        check(lp[s], rl, *TOL[dtype], "lse_part " + tag)
         empty = ~np.isfinite(rl)
         assert np.all(op[s][empty] == 0.0), "o_part of empty states must be 0: " + tag
-        check(op[s][~empty], ro[~empty], *BF16, "o_part " + tag)
+        check(op[s][~empty], ro[~empty], *TOL[dtype], "o_part " + tag)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("case", SPLIT_CASES)
-def test_split_and_merge_match_the_full_oracle(fa, oracle, case):
+def test_split_and_merge_match_the_full_oracle(fa, oracle, case, dtype):
     B, Hq, Hkv, Nq, Nk, d, causal, S = case
-    q, k, v = _case_inputs(B, Hq, Hkv, Nq, Nk, d, 3000 + Nq + Nk + S)
+    q, k, v = _case_inputs(B, Hq, Hkv, Nq, Nk, d, 3000 + Nq + Nk + S, dtype)
     sc = 1.0 / math.sqrt(d)
-    print("splitkv + merge", case, flush=True)
+    print("splitkv + merge", case, dtype, flush=True)
     o, lse = fa.attention_kv(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=sc, num_splits=S)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_kv(q, k, v, causal=causal, scale=sc)
-    assert o.dtype == torch.bfloat16
-    check(o.float().cpu().numpy(), ro, *BF16, "O %s" % (case,))
-    check(lse.cpu().numpy(), rl, *BF16, "LSE %s" % (case,))
+    assert o.dtype == q.dtype
+    check(o.float().cpu().numpy(), ro, *TOL[dtype], "O %s %s" % (case, dtype))
+    check(lse.cpu().numpy(), rl, *TOL[dtype], "LSE %s %s" % (case, dtype))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_one_range_equals_the_forward_bitwise(fa, d, causal):
+def test_one_range_equals_the_forward_bitwise(fa, d, causal, dtype):
     """S = 1 over a square problem: the same state, normalised once, then merged with weight 1."""
-    q, k, v = fin.make_qkv(2, 4, 2, 333, d, "bf16", 4000 + d)
+    q, k, v = fin.make_qkv(2, 4, 2, 333, d, dtype, 4000 + d)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     print("split S=1 vs forward d=%d causal=%d" % (d, causal), flush=True)
     o_ref, l_ref = fa.forward(qd, kd, vd, causal=causal)
@@ -124,7 +130,7 @@ def test_one_range_equals_the_forward_bitwise(fa, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_merge_kernel_matches_the_pages_merge(fa, oracle, d, out_dtype):
     S, B, H, N = 6, 2, 3, 50
     rng = np.random.default_rng(5000 + d)
@@ -138,7 +144,7 @@ def test_merge_kernel_matches_the_pages_merge(fa, oracle, d, out_dtype):
     o, lse = fa.merge(torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda(), out_dtype=out_dtype)
     torch.cuda.synchronize()
     ro, rl = oracle.merge_partials(o_part, lse_part)
-    tol_o = (2e-6, 2e-6) if out_dtype == torch.float32 else BF16
+    tol_o = {torch.float32: (2e-6, 2e-6), torch.bfloat16: BF16, torch.float16: F16}[out_dtype]
     check(o.float().cpu().numpy(), ro, *tol_o, "merged o")
     check(lse.cpu().numpy(), rl, 2e-6, 2e-6, "merged lse")
     assert lse[0, 0, 0].item() == -math.inf and torch.all(o[0, 0, 0] == 0)

@@ -1,6 +1,6 @@
 """Static checks on the gfx950 code the kernels compile to (CPU only: hipcc here).
 
-The bf16 kernel stages K/V tiles with loads that write LDS directly
+The 16-bit (bf16 and fp16) kernel stages K/V tiles with loads that write LDS directly
 (buffer_load ... lds).  Those loads count in vmcnt, and a workgroup barrier does
 not by itself wait for them: every s_barrier must therefore follow an s_waitcnt
 that includes vmcnt(0), or a wave could pass the barrier while its part of the
@@ -25,13 +25,13 @@ def bf16_asm(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("isa") / "bf16.s")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
                     "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
-                    "--offload-device-only", "-S", os.path.join(CSRC, "fa_fwd_bf16.hip"), "-o", out],
+                    "--offload-device-only", "-S", os.path.join(CSRC, "fa_fwd_mfma16.hip"), "-o", out],
                    check=True, capture_output=True)
     return open(out).read()
 
 
 def kernels(asm):
-    for name in re.findall(r"^(_ZN2fa15fwd_bf16_kernel\S+):", asm, re.M):
+    for name in re.findall(r"^(_ZN2fa12fwd16_kernel\S+):", asm, re.M):
         i = asm.index(name + ":")
         j = asm.index(".Lfunc_end", i)
         body = [l.strip() for l in asm[i:j].splitlines()]
@@ -46,7 +46,7 @@ def test_every_barrier_waits_for_lds_dma(bf16_asm):
         for n, x in enumerate(ins):
             if x.startswith("s_barrier"):
                 assert ins[n - 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[n - 1], (name, n, ins[n - 1])
-    assert found >= 8
+    assert found >= 24      # bf16 and fp16: 8 square and 4 split instantiations each
 
 
 def test_no_packed_fp32_and_no_scratch(bf16_asm):
