@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "f16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_mfma16.hip",
     "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
     "merge": "flashattention_online_softmax_fwd_amd/csrc/fa_merge.hip",
+    "softmax": "flashattention_online_softmax_fwd_amd/csrc/fa_softmax.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -285,6 +286,81 @@ def run_kv_workload(name, steps, warmup):
     }
 
 
+# Reads and writes per element of each row-softmax algorithm (spicyshark.co lesson, "The cost:
+# three passes" and "Why reading once matters").
+SOFTMAX_ACCESSES = {"online": (2, 1), "safe": (3, 1)}
+
+
+def run_softmax_workload(name, steps, warmup):
+    """Row softmax of a [rows, cols] matrix by both algorithms; one step is one launch.
+
+    Each algorithm is priced against HBM with its own access count (the bytes it
+    must move if nothing stays on chip between its passes); ``value`` is the
+    online algorithm's effective rate, x read once plus y written once, over its
+    wall time.
+    """
+    import torch
+
+    import flashattention_online_softmax_fwd_amd as fa
+    from flashattention_online_softmax_fwd_amd import _lib
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+
+    fa.load_library()
+    w = fin.SOFTMAX_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    x = fin.softmax_workload_inputs(w).to(dev)
+    y = torch.empty_like(x)
+    lse = torch.empty((w.rows,), dtype=torch.float32, device=dev)
+    dt = {"f32": _lib.FA_DTYPE_F32, "bf16": _lib.FA_DTYPE_BF16, "f16": _lib.FA_DTYPE_F16}[w.dtype]
+    stream = torch.cuda.current_stream()
+    out = {}
+    for algo, code in (("online", _lib.FA_SOFTMAX_ONLINE), ("safe", _lib.FA_SOFTMAX_SAFE)):
+        def call():
+            rc = _lib.fa_softmax(x.data_ptr(), y.data_ptr(), lse.data_ptr(), w.rows, w.cols, dt, code,
+                                 stream.cuda_stream)
+            assert rc == 0, _lib.fa_last_error()
+        for _ in range(warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        reads, writes = SOFTMAX_ACCESSES[algo]
+        nbytes = (reads + writes) * w.rows * w.cols * w.esize + 4 * w.rows
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[algo] = {"wall_s": wall, "ms": ms, "roofline": {
+            "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": traffic_for(w.name + ":" + algo, "softmax"), "kernel": "fa::softmax_kernel (%s)" % algo,
+            "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes,
+            "accesses_per_element": reads + writes}}
+    on, sa = out["online"], out["safe"]
+    return {
+        "metric": "row softmax effective GB/s (x read once, y written once), online algorithm",
+        "value": w.io_bytes * steps / on["wall_s"] / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": on["wall_s"] * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal scores x %g, numpy default_rng(%d))" % (w.sigma, w.seed),
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "dtype": w.dtype,
+                   "io_bytes_per_step": w.io_bytes},
+        "roofline": on["roofline"],
+        "safe_roofline": sa["roofline"],
+        "online_speedup_over_safe": sa["ms"] / on["ms"],
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,7 +369,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None,
-                    help="one of inputs.WORKLOADS or inputs.KV_WORKLOADS (default: the metric's)")
+                    help="one of inputs.WORKLOADS, KV_WORKLOADS or SOFTMAX_WORKLOADS (default: the metric's)")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -318,10 +394,14 @@ def main(argv=None):
             print(json.dumps(run_workload(name, args.steps, args.warmup, False, 0.0)), flush=True)
         for name in fin.KV_WORKLOADS:
             print(json.dumps(run_kv_workload(name, args.steps, args.warmup)), flush=True)
+        for name in fin.SOFTMAX_WORKLOADS:
+            print(json.dumps(run_softmax_workload(name, args.steps, args.warmup)), flush=True)
         return 0
     name = args.workload or fin.BENCH_WORKLOAD
     if name in fin.KV_WORKLOADS:
         rec = run_kv_workload(name, args.steps, args.warmup)
+    elif name in fin.SOFTMAX_WORKLOADS:
+        rec = run_softmax_workload(name, args.steps, args.warmup)
     else:
         rec = run_workload(name, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
     if args.copy_calibration:

@@ -17,12 +17,13 @@ import torch
 
 from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FA_ERR_HIP, FA_ERR_INVALID_ARG,
-                   FA_ERR_UNSUPPORTED, FA_OK, LibraryNotBuilt, fa_abi_version, fa_error_string,
-                   fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error, fa_merge, fa_split_chunk,
-                   fa_splitkv_num_splits, fa_tile_shapes)
+                   FA_ERR_UNSUPPORTED, FA_OK, FA_SOFTMAX_ONLINE, FA_SOFTMAX_SAFE, LibraryNotBuilt,
+                   fa_abi_version, fa_error_string, fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error,
+                   fa_merge, fa_softmax, fa_split_chunk, fa_splitkv_num_splits, fa_tile_shapes)
 
-__all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "fa_fwd", "fa_fwd_tiled",
-           "fa_fwd_splitkv", "fa_merge", "fa_split_chunk", "fa_splitkv_num_splits",
+__all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "softmax", "fa_fwd", "fa_fwd_tiled",
+           "fa_fwd_splitkv", "fa_merge", "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax",
+           "FA_SOFTMAX_ONLINE", "FA_SOFTMAX_SAFE",
            "fa_tile_shapes", "fa_error_string",
            "fa_last_error", "fa_abi_version", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16",
@@ -200,3 +201,41 @@ def attention_kv(q, k, v, causal=False, scale=None, num_splits=None):
         num_splits = max(1, fa_splitkv_num_splits(B, Hq, Hkv, max(Nq, 1), max(Nk, 1)))
     o_part, lse_part = forward_splitkv(q, k, v, num_splits, causal=causal, scale=scale)
     return merge(o_part, lse_part, out_dtype=q.dtype)
+
+
+_ALGOS = {"online": FA_SOFTMAX_ONLINE, "safe": FA_SOFTMAX_SAFE}
+
+
+def softmax(x, algo="online", out=None, lse=None):
+    """Softmax over the last dimension of a contiguous CUDA tensor (float32, bfloat16 or float16).
+
+    algo "online": the running max and sum in one read of each row, then the
+    output (2 reads + 1 write per element); "safe": max, sum, output (3 reads +
+    1 write).  Returns (y like x, lse float32 of x's shape without its last
+    dimension).  ``out`` may be x itself (in place).
+    """
+    lib = _lib.load()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous CUDA tensor with at least one dimension")
+    if x.dtype not in _DTYPES:
+        raise ValueError("dtype %s is not supported" % x.dtype)
+    if algo not in _ALGOS:
+        raise ValueError("algo must be 'online' or 'safe'")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    if lse is None:
+        lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    elif (lse.shape != x.shape[:-1] or lse.dtype != torch.float32 or lse.device != x.device
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of x's shape without its last dimension")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.fa_softmax(x.data_ptr(), out.data_ptr(), lse.data_ptr() if rows else None, rows, cols,
+                            _DTYPES[x.dtype], _ALGOS[algo], stream)
+    if rc != FA_OK:
+        _raise(rc)
+    return out, lse

@@ -24,6 +24,9 @@ FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F16 = 2
 
+FA_SOFTMAX_ONLINE = 0
+FA_SOFTMAX_SAFE = 1
+
 # name -> (restype, argtypes), mirroring include/fa.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -36,6 +39,7 @@ SIGNATURES = {
     "fa_merge": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fa_split_chunk": (_I, [_I, _I]),
     "fa_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "fa_softmax": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _I, _I, _P]),
     "fa_error_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (_I, []),
@@ -90,6 +94,10 @@ def fa_split_chunk(Nk, num_splits):
 
 def fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk):
     return load().fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk)
+
+
+def fa_softmax(x, y, lse, rows, cols, dtype, algo, stream):
+    return load().fa_softmax(x, y, lse, rows, cols, dtype, algo, stream)
 
 
 def fa_tile_shapes(dtype, d):

@@ -261,9 +261,48 @@ int run_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
     return FA_OK;
 }
 
+int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, int dtype, int algo, void* stream)
+{
+    g_last_error.clear();
+    if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (algo != FA_SOFTMAX_ONLINE && algo != FA_SOFTMAX_SAFE)
+        return fail(FA_ERR_INVALID_ARG, "algo must be FA_SOFTMAX_ONLINE or FA_SOFTMAX_SAFE");
+    if (rows < 0 || cols < 0) return fail(FA_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (rows == 0) return FA_OK;
+    if (cols == 0) return fail(FA_ERR_INVALID_ARG, "a row needs at least one entry (cols >= 1)");
+    if (rows > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "more than 2^31 - 1 rows");
+    if (!x || !y) return fail(FA_ERR_INVALID_ARG, "null pointer");
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(y) % 16 != 0 ||
+        (lse && reinterpret_cast<uintptr_t>(lse) % 16 != 0))
+        return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * (dtype == FA_DTYPE_F32 ? 4 : 2);
+    if (bytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
+    if (x != y && overlaps(x, bytes, y, bytes))
+        return fail(FA_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    if (lse && (overlaps(lse, (uint64_t)rows * 4, x, bytes) || overlaps(lse, (uint64_t)rows * 4, y, bytes)))
+        return fail(FA_ERR_INVALID_ARG, "lse must not overlap x or y");
+    fa::SoftmaxParams p;
+    p.x = x;
+    p.y = y;
+    p.lse = lse;
+    p.rows = rows;
+    p.cols = cols;
+    p.dtype = dtype;
+    p.online = algo == FA_SOFTMAX_ONLINE;
+    const hipError_t err = fa::launch_softmax(p, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_softmax(const void* x, void* y, float* lse, long long rows, int cols, int dtype, int algo, void* stream)
+{
+    return run_softmax(x, y, lse, rows, cols, dtype, algo, stream);
+}
+
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int N, int d, int causal, float scale, int dtype, void* stream)
@@ -352,7 +391,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 2;
+    return 3;
 }
 
 }  // extern "C"

@@ -60,4 +60,16 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream);   // FA_DTYPE_*
 
+// Row softmax: y [rows][cols] = softmax of each row of x, lse [rows] (optional).
+struct SoftmaxParams {
+    const void* x;
+    void* y;
+    float* lse;        // may be null
+    long long rows;    // <= 2^31 - 1 (one workgroup per row)
+    int cols;
+    int dtype;         // FA_DTYPE_*: x and y
+    bool online;       // true: running max and sum in one pass; false: three passes
+};
+hipError_t launch_softmax(const SoftmaxParams& p, hipStream_t stream);
+
 }  // namespace fa

@@ -125,6 +125,52 @@ KV_WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    """A [rows, cols] matrix of scores drawn N(0, sigma^2), softmaxed row by row."""
+    name: str
+    rows: int
+    cols: int
+    dtype: str
+    seed: int = 0
+    sigma: float = 4.0
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def io_bytes(self) -> int:
+        """x read once and y written once: the least any softmax must move."""
+        return 2 * self.rows * self.cols * self.esize
+
+
+# Scores N(0, 4^2) like the pages' random test of the online update.  Long rows (each
+# pass over a row goes to HBM: 1 MiB or 256 KiB per row, far more rows in flight than
+# the caches hold) and short rows (a 16 KiB row stays in L2 between its passes).
+SOFTMAX_WORKLOADS = {
+    "s1_f32_softmax_r1024_c262144": SoftmaxWorkload("s1_f32_softmax_r1024_c262144", 1024, 262144, "f32",
+                                                    seed=1201),
+    "s2_f32_softmax_r65536_c4096": SoftmaxWorkload("s2_f32_softmax_r65536_c4096", 65536, 4096, "f32",
+                                                   seed=1202),
+    "s3_bf16_softmax_r4096_c131072": SoftmaxWorkload("s3_bf16_softmax_r4096_c131072", 4096, 131072, "bf16",
+                                                     seed=1203),
+}
+
+
+def make_scores(rows, cols, dtype="f32", seed=0, sigma=4.0):
+    """Seeded [rows, cols] scores N(0, sigma^2) as a CPU torch tensor in the dtype."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return torch.from_numpy(x).to(torch_dtype(dtype))
+
+
+def softmax_workload_inputs(w: SoftmaxWorkload):
+    return make_scores(w.rows, w.cols, w.dtype, w.seed, w.sigma)
+
+
 def kv_workload_inputs(w: KVWorkload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.d, w.dtype, w.seed, 1.0, Nk=w.Nk)
 

@@ -168,13 +168,40 @@ int fa_split_chunk(int Nk, int num_splits);
  * heads that share one K/V head), or -1 for a bad size. */
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
 
+/* Algorithms of fa_softmax. */
+enum {
+    FA_SOFTMAX_ONLINE = 0,   /* running max and sum in one read, then the output: 2 reads + 1 write */
+    FA_SOFTMAX_SAFE = 1      /* max, then sum, then the output: 3 reads + 1 write                 */
+};
+
+/*
+ * fa_softmax: the softmax of every row of a matrix,
+ *     y[r][j] = exp(x[r][j] - m_r) / l_r,   m_r = max_j x[r][j],
+ *     l_r = sum_j exp(x[r][j] - m_r),       lse[r] = m_r + ln l_r,
+ * the safe softmax of the pages (spicyshark.co online-softmax lesson, "The fix:
+ * subtract the maximum").  algo picks how often each row is read ("The cost: three
+ * passes"; "Why reading once matters"; "The idea" for the running max and sum
+ * that the online form keeps, the update of Milakov and Gimelshein the pages cite).
+ *
+ *   x, y      device pointers, [rows][cols] contiguous, dtype FA_DTYPE_F32,
+ *             FA_DTYPE_BF16 or FA_DTYPE_F16 (both the same dtype; the arithmetic is
+ *             fp32); y may be x itself (in place) but must not otherwise overlap it
+ *   lse       device pointer, [rows] float32, written; may be NULL
+ *   rows      0 .. 2^31 - 1 (0: FA_OK, nothing touched); cols >= 1
+ *   algo      FA_SOFTMAX_ONLINE or FA_SOFTMAX_SAFE (same result up to rounding)
+ * A row whose entries are all -inf has no softmax: its y is nan and its lse -inf.
+ * Ownership, alignment (16 bytes for x, y and lse) and error rules as for fa_fwd.
+ */
+int fa_softmax(const void* x, void* y, float* lse, long long rows, int cols, int dtype, int algo,
+               void* stream);
+
 /* Static text for a return code. */
 const char* fa_error_string(int code);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

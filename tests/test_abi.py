@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
                           "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
-                          "fa_split_chunk", "fa_splitkv_num_splits"}
+                          "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -64,7 +64,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -181,3 +181,24 @@ def test_split_chunk_and_default_splits(lib):
     assert lib.fa_splitkv_num_splits(8, 32, 8, 1, 32768) == 16
     assert lib.fa_splitkv_num_splits(0, 1, 1, 1, 1) == -1
     assert lib.fa_splitkv_num_splits(1, 3, 2, 1, 1) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, P + 0x100000, 0, 4, 64, 0, 0), 1),                   # null x
+    ((P, P + 0x100000, 0, 4, 64, 5, 0), 1),                   # unknown dtype
+    ((P, P + 0x100000, 0, 4, 64, 0, 2), 1),                   # unknown algorithm
+    ((P, P + 0x100000, 0, -1, 64, 0, 0), 1),                  # negative rows
+    ((P, P + 0x100000, 0, 4, 0, 0, 0), 1),                    # empty rows
+    ((P, P + 4, 0, 4, 64, 0, 0), 1),                          # misaligned y
+    ((P, P + 0x40, 0, 4, 64, 0, 0), 1),                       # y overlaps x without being x
+    ((P, P + 0x100000, P + 0x20, 4, 64, 0, 0), 1),            # lse overlaps x
+    ((P, P + 0x100000, 0, 1 << 31, 64, 0, 0), 2),             # too many rows for the grid
+])
+def test_softmax_rejects_bad_arguments(lib, args, code):
+    assert lib.fa_softmax(*args, None) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_softmax_empty_matrix_is_ok(lib):
+    assert lib.fa_softmax(0, 0, 0, 0, 64, 0, 0, None) == 0
+    assert lib.fa_softmax(0, 0, 0, 0, 0, 1, 1, None) == 0

@@ -1,0 +1,125 @@
+"""The row-softmax kernel (fa_softmax) on the GPU, against the fp64 oracle.
+
+Both algorithms (online: running max and sum in one read; safe: max, sum,
+output) are compared element by element with ``softmax_oracle.softmax_rows``
+on the same rounded inputs.  Tolerance, derived from the arithmetic (fp32
+throughout, one exponential per element, per-thread sums of at most a few
+thousand positive terms, then the rounding of y to its dtype):
+    fp32   |y - r| <= 3e-5 |r| + 1.2e-38
+    bf16   |y - r| <= 4e-3 |r| + 1.2e-38 (RNE to bf16 costs up to 2^-9)
+    fp16   |y - r| <= 5e-4 |r| + 3e-8    (RNE to fp16; 3e-8 is half its subnormal step)
+    lse    |lse - r| <= 3e-5 + 1e-6 |r|  for every dtype (lse is fp32)
+1.2e-38 is fp32's smallest normal number: shares below it are flushed to zero by the
+exponential, as any fp32 softmax does far from the max.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from flashattention_online_softmax_fwd_amd import inputs as fin
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1.2e-38, 3e-5), "bf16": (1.2e-38, 4e-3), "f16": (3e-8, 5e-4)}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import flashattention_online_softmax_fwd_amd as fa_mod
+    fa_mod.load_library()
+    return fa_mod
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    from oracle import softmax_oracle
+    return softmax_oracle
+
+
+def check(y, lse, ry, rl, dtype, what):
+    y = np.asarray(y, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    atol, rtol = TOL[dtype]
+    assert np.array_equal(np.isnan(y), np.isnan(ry)), what + ": nan pattern"
+    ok = ~np.isnan(ry)
+    err = np.abs(y[ok] - ry[ok])
+    bad = err > atol + rtol * np.abs(ry[ok])
+    assert not bad.any(), "%s: %d of %d outside tolerance, max abs err %.3e" % (what, bad.sum(), bad.size, err.max())
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl)), what + ": -inf pattern of lse"
+    f = np.isfinite(rl)
+    assert np.all(np.abs(lse[f] - rl[f]) <= 3e-5 + 1e-6 * np.abs(rl[f])), what + ": lse"
+
+
+def run(fa, x, algo):
+    y, lse = fa.softmax(x.cuda(), algo=algo)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), lse.cpu().numpy()
+
+
+SHAPES = [(1, 1), (3, 5), (7, 13), (4, 256), (5, 1023), (3, 1024), (2, 4097), (6, 33000), (2, 65536)]
+
+
+@pytest.mark.parametrize("algo", ["online", "safe"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_matches_the_oracle(fa, oracle, shape, dtype, algo):
+    rows, cols = shape
+    x = fin.make_scores(rows, cols, dtype, seed=rows * 7 + cols)
+    print("softmax", shape, dtype, algo, flush=True)
+    y, lse = run(fa, x, algo)
+    ry, rl = oracle.softmax_rows(x)
+    check(y, lse, ry, rl, dtype, "%s %s %s" % (shape, dtype, algo))
+
+
+@pytest.mark.parametrize("algo", ["online", "safe"])
+def test_masked_entries_large_scores_and_empty_rows(fa, oracle, algo):
+    x = torch.full((5, 300), -math.inf)
+    x[0, :3] = torch.tensor([1000.0, 1001.0, 1002.0])          # the pages' overflow example
+    x[1, ::7] = torch.linspace(-5, 5, 43)                      # most entries masked
+    x[2, 299] = 0.0                                            # one visible entry: y is one-hot
+    x[3] = torch.from_numpy(np.random.default_rng(1).standard_normal(300).astype(np.float32)) * 30
+    # row 4 stays all -inf: no softmax (nan), lse -inf
+    y, lse = run(fa, x, algo)
+    ry, rl = oracle.softmax_rows(x)
+    check(y, lse, ry, rl, "f32", "masked " + algo)
+    assert y[2, 299] == 1.0 and np.all(y[2, :299] == 0.0)
+    assert np.all(np.isnan(y[4])) and lse[4] == -math.inf
+
+
+def test_the_two_algorithms_agree(fa):
+    x = fin.make_scores(64, 20000, "f32", seed=9)
+    a = run(fa, x, "online")
+    b = run(fa, x, "safe")
+    assert np.allclose(a[0], b[0], rtol=3e-5, atol=0) and np.allclose(a[1], b[1], rtol=0, atol=3e-5)
+
+
+@pytest.mark.parametrize("algo", ["online", "safe"])
+def test_in_place_and_deterministic(fa, algo):
+    x = fin.make_scores(33, 3000, "bf16", seed=10).cuda()
+    y, lse = fa.softmax(x, algo=algo)
+    y2, lse2 = fa.softmax(x, algo=algo)
+    xi = x.clone()
+    fa.softmax(xi, algo=algo, out=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(lse, lse2) and torch.equal(xi, y)
+
+
+@pytest.mark.parametrize("algo", ["online", "safe"])
+@pytest.mark.parametrize("name", sorted(fin.SOFTMAX_WORKLOADS))
+def test_measured_workloads_at_full_size(fa, oracle, name, algo):
+    w = fin.SOFTMAX_WORKLOADS[name]
+    x = fin.softmax_workload_inputs(w)
+    print("full-size softmax", name, algo, flush=True)
+    y, lse = fa.softmax(x.cuda(), algo=algo)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, w.rows - 1], np.random.default_rng(w.seed).choice(w.rows, 30, replace=False)]))
+    yr = y[torch.as_tensor(rows, device=y.device)].float().cpu().numpy()
+    lr = lse.cpu().numpy()[rows]
+    ry, rl = oracle.softmax_rows(x[torch.as_tensor(rows)])
+    check(yr, lr, ry, rl, w.dtype, name + " " + algo)
+    s = y.float().sum(dim=1)
+    assert torch.all(torch.abs(s - 1) < (2e-2 if w.dtype == "bf16" else 1e-3)).item()

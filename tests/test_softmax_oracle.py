@@ -89,3 +89,9 @@ def test_reading_counts_of_the_two_algorithms():
     rw = g["reads_and_writes_per_element"]
     assert acc["safe"] == sum(rw["safe"]) and acc["online"] == sum(rw["online"])
     assert abs(acc["safe"] / acc["online"] - 4 / 3) < 1e-12 and g["reported_speedup_up_to"] <= 4 / 3 + 0.01
+
+
+def test_bench_prices_each_algorithm_with_the_pages_access_counts():
+    import bench
+    g = _golden("p4_reading_once.json")
+    assert {k: list(v) for k, v in bench.SOFTMAX_ACCESSES.items()} == g["reads_and_writes_per_element"]
