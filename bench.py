@@ -42,6 +42,7 @@ KERNEL_SOURCES = {
     "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
     "merge": "flashattention_online_softmax_fwd_amd/csrc/fa_merge.hip",
     "softmax": "flashattention_online_softmax_fwd_amd/csrc/fa_softmax.hip",
+    "bwd": "flashattention_online_softmax_fwd_amd/csrc/fa_bwd_mfma16.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -361,6 +362,76 @@ def run_softmax_workload(name, steps, warmup):
     }
 
 
+def run_bwd_workload(name, steps, warmup):
+    """Backward pass (dq, dk, dv from q, k, v, o, lse and dO); one step is one fa_bwd
+    call, its three kernels (delta, dq, dk/dv) back to back on one stream.
+
+    ``value`` counts the five products of the backward (S, dP, dV, dK, dQ: 2.5 times
+    the forward's flops) per step over the timed wall time.  The kernels recompute S
+    and dP once more (in the dq kernel and in the dk/dv kernel), which the count
+    leaves out.  ``roofline`` prices the call's average duration, from HIP events on
+    its stream, against the dense bf16 MFMA peak; the per-kernel split is in the
+    rocprofv3 summary.
+    """
+    import torch
+
+    import flashattention_online_softmax_fwd_amd as fa
+    from flashattention_online_softmax_fwd_amd import _lib
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+
+    fa.load_library()
+    w = fin.BWD_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in fin.bwd_workload_inputs(w))
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.softmax_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    dt = {"bf16": _lib.FA_DTYPE_BF16, "f16": _lib.FA_DTYPE_F16}[w.dtype]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        rc = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), w.B, w.Hq, w.Hkv, w.N,
+                         w.d, int(w.causal), w.softmax_scale, dt, stream.cuda_stream)
+        assert rc == 0, _lib.fa_last_error()
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = fin.bwd_flops(w)
+    achieved = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {
+        "metric": "attention bwd TFLOP/s (5 products, 2.5x the forward's flops)",
+        "value": flops * steps / wall / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": wall * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/K/V/dO, numpy default_rng(%d), dO seed + 50000)" % w.seed,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_for(w.name, "bwd"),
+                     "kernel": "fa_bwd (fa::bwd_delta_kernel + fa::bwd_dq_kernel + fa::bwd_dkdv_kernel)",
+                     "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,7 +440,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None,
-                    help="one of inputs.WORKLOADS, KV_WORKLOADS or SOFTMAX_WORKLOADS (default: the metric's)")
+                    help="one of inputs.WORKLOADS, KV_WORKLOADS, SOFTMAX_WORKLOADS or BWD_WORKLOADS "
+                         "(default: the metric's)")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -396,12 +468,16 @@ def main(argv=None):
             print(json.dumps(run_kv_workload(name, args.steps, args.warmup)), flush=True)
         for name in fin.SOFTMAX_WORKLOADS:
             print(json.dumps(run_softmax_workload(name, args.steps, args.warmup)), flush=True)
+        for name in fin.BWD_WORKLOADS:
+            print(json.dumps(run_bwd_workload(name, args.steps, args.warmup)), flush=True)
         return 0
     name = args.workload or fin.BENCH_WORKLOAD
     if name in fin.KV_WORKLOADS:
         rec = run_kv_workload(name, args.steps, args.warmup)
     elif name in fin.SOFTMAX_WORKLOADS:
         rec = run_softmax_workload(name, args.steps, args.warmup)
+    elif name in fin.BWD_WORKLOADS:
+        rec = run_bwd_workload(name, args.steps, args.warmup)
     else:
         rec = run_workload(name, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
     if args.copy_calibration:

@@ -4,8 +4,10 @@
 the HIP kernels in libfa.so (C ABI in include/fa.h).  ``forward_splitkv`` and
 ``merge`` split the keys into ranges, compute each range's partial state and
 combine them; ``attention_kv`` does both for queries that are the last Nq of Nk
-positions (e.g. decoding against a cache).  torch supplies device memory and the
-stream; every step of the attention runs in the kernels.
+positions (e.g. decoding against a cache).  ``softmax`` is the row softmax on
+its own.  ``backward`` gives dq, dk, dv from the forward's o and lse, and
+``attention`` wraps forward and backward as a torch autograd function.  torch
+supplies device memory and the stream; every step runs in the kernels.
 
 The library is loaded on first use, and a missing build raises.
 """
@@ -18,10 +20,11 @@ import torch
 from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FA_ERR_HIP, FA_ERR_INVALID_ARG,
                    FA_ERR_UNSUPPORTED, FA_OK, FA_SOFTMAX_ONLINE, FA_SOFTMAX_SAFE, LibraryNotBuilt,
-                   fa_abi_version, fa_error_string, fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error,
+                   fa_abi_version, fa_bwd, fa_error_string, fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error,
                    fa_merge, fa_softmax, fa_split_chunk, fa_splitkv_num_splits, fa_tile_shapes)
 
-__all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "softmax", "fa_fwd", "fa_fwd_tiled",
+__all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "softmax", "backward", "attention",
+           "fa_fwd", "fa_fwd_tiled", "fa_bwd",
            "fa_fwd_splitkv", "fa_merge", "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax",
            "FA_SOFTMAX_ONLINE", "FA_SOFTMAX_SAFE",
            "fa_tile_shapes", "fa_error_string",
@@ -239,3 +242,74 @@ def softmax(x, algo="online", out=None, lse=None):
     if rc != FA_OK:
         _raise(rc)
     return out, lse
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None, delta=None):
+    """Gradients of the square attention forward: returns (dq, dk, dv, delta).
+
+    q, o, do [B, Hq, N, d] and k, v [B, Hkv, N, d] bfloat16 or float16 CUDA tensors,
+    contiguous; o and lse [B, Hq, N] float32 as ``forward`` returned them for the same
+    q, k, v, causal and scale.  delta [B, Hq, N] float32 is rowsum(do * o).  dk and
+    dv of a K/V head sum over the query heads that read it.  The gradient buffers
+    may be given to write into existing tensors.  Runs on torch's current stream.
+    """
+    lib = _lib.load()
+    _check_inputs(q, k, v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != N:
+        raise ValueError("the backward is for the square problem: k and v need N = %d rows" % N)
+    for name, t in (("o", o), ("do", do)):
+        if (not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype
+                or t.device != q.device or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous tensor like q" % name)
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N] on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def _out(t, like, name):
+        if t is None:
+            return torch.empty_like(like)
+        if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor like %s" % (name, "q" if like is q else "k"))
+        return t
+
+    dq, dk, dv = _out(dq, q, "dq"), _out(dk, k, "dk"), _out(dv, v, "dv")
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif (delta.shape != (B, Hq, N) or delta.dtype != torch.float32 or delta.device != q.device
+          or not delta.is_contiguous()):
+        raise ValueError("delta must be a contiguous float32 tensor [B, Hq, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, N, d,
+                        int(bool(causal)), float(scale), _DTYPES[q.dtype], stream)
+    if rc != FA_OK:
+        _raise(rc)
+    return dq, dk, dv, delta
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = forward(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv, _ = backward(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal=False, scale=None):
+    """softmax(scale q k^T) v with autograd: the forward saves (o, lse), the backward
+    recomputes the weights from them (bfloat16 or float16 inputs for the backward)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _Attention.apply(q, k, v, bool(causal), float(scale))

@@ -40,6 +40,7 @@ SIGNATURES = {
     "fa_split_chunk": (_I, [_I, _I]),
     "fa_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_softmax": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _I, _I, _P]),
+    "fa_bwd": (_I, [_P] * 10 + [_I] * 6 + [ctypes.c_float, _I, _P]),
     "fa_error_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (_I, []),
@@ -98,6 +99,11 @@ def fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk):
 
 def fa_softmax(x, y, lse, rows, cols, dtype, algo, stream):
     return load().fa_softmax(x, y, lse, rows, cols, dtype, algo, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype, stream):
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype,
+                         stream)
 
 
 def fa_tile_shapes(dtype, d):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_host.cpp", "fa_fwd_mfma16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_softmax.hip"]
+SOURCES = ["fa_host.cpp", "fa_fwd_mfma16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_softmax.hip", "fa_bwd_mfma16.hip"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.

@@ -50,99 +50,12 @@
 // and because that offset is arbitrary a wave's diagonal may straddle two key
 // tiles, so causal split kernels also check the mask on tiles before the last.
 #include "fa_kernels.h"
+#include "fa_mfma16_common.h"
 
 #include <float.h>
 #include <stdint.h>
 
 namespace fa {
-
-// The element type's MFMA, pair dot product and vector types.  fp16's largest value,
-// 65504, is never approached: P stays below 2^8 (see the lazy rescale above), scores
-// and O are fp32 until the final rounding.
-template <typename E>
-struct Elem;
-template <>
-struct Elem<__bf16> {
-    typedef __attribute__((ext_vector_type(8))) __bf16 x8;
-    typedef __attribute__((ext_vector_type(4))) __bf16 x4;
-    typedef __attribute__((ext_vector_type(2))) __bf16 x2;
-    static __device__ __forceinline__ __attribute__((ext_vector_type(16))) float
-    mfma(x8 a, x8 b, __attribute__((ext_vector_type(16))) float c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float dot2(x2 a, x2 b, float c)
-    {
-        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
-    }
-};
-template <>
-struct Elem<_Float16> {
-    typedef __attribute__((ext_vector_type(8))) _Float16 x8;
-    typedef __attribute__((ext_vector_type(4))) _Float16 x4;
-    typedef __attribute__((ext_vector_type(2))) _Float16 x2;
-    static __device__ __forceinline__ __attribute__((ext_vector_type(16))) float
-    mfma(x8 a, x8 b, __attribute__((ext_vector_type(16))) float c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ float dot2(x2 a, x2 b, float c)
-    {
-        return __builtin_amdgcn_fdot2(a, b, c, false);
-    }
-};
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
-
-#define FA_LDS __attribute__((address_space(3)))
-
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kRescaleSlack = 8.0f;   // log2 units: P may grow to 2^8 before m moves
-
-// XOR mask for the 16-byte chunks of K/V tile row r.  Chosen so that both LDS read
-// patterns are free of bank conflicts: 16 consecutive rows at one logical chunk
-// (the K operand) and 4 consecutive rows x 4 consecutive chunks (the V operand).
-template <int D>
-__device__ __forceinline__ int swz(int r)
-{
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);   // D == 64: 8 chunks, 2 rows per bank row
-}
-
-// Reductions over the two lane halves, which hold the same query row.
-__device__ __forceinline__ float lane_half_max(float x)
-{
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-
-__device__ __forceinline__ float lane_half_sum(float x)
-{
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-// The tile barrier.  Loads that write LDS directly (buffer_load ... lds) count in
-// vmcnt, and a workgroup barrier does not by itself wait for them, so each wave
-// first waits for its own tile loads to land; after the barrier every wave's loads
-// have, and the whole tile is visible.
-__device__ __forceinline__ void tile_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
-    __syncthreads();
-}
-
-template <bool V>
-struct Flag {
-    static constexpr bool value = V;
-};
-
-template <int V>
-struct Int {
-    static constexpr int value = V;
-};
 
 template <typename E, int D, int BM, int BN, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -294,6 +294,77 @@ int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, in
     return FA_OK;
 }
 
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+            void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int N, int d, int causal,
+            float scale, int dtype, void* stream)
+{
+    g_last_error.clear();
+    if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
+    if (dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "the backward is built for 16-bit inputs only");
+    if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
+    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (!std::isfinite((float)((double)scale * 1.4426950408889634)))
+        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
+    if (B == 0 || N == 0) return FA_OK;
+
+    const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+    for (const void* ptr : ptrs)
+        if (!ptr) return fail(FA_ERR_INVALID_ARG, "null pointer");
+    for (const void* ptr : ptrs)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const uint64_t qrows = (uint64_t)B * (uint64_t)Hq * (uint64_t)N;
+    const uint64_t qbytes = qrows * (uint64_t)d * 2;
+    const uint64_t kvbytes = (uint64_t)B * (uint64_t)Hkv * (uint64_t)N * (uint64_t)d * 2;
+    const uint64_t lbytes = qrows * 4;
+    if (qbytes >> 62 || kvbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
+    if ((uint64_t)N * (uint64_t)d * 2 > 0x7fffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "one head of a tensor exceeds 2 GiB");
+    const void* in[6] = {q, k, v, o, lse, dout};
+    const uint64_t in_n[6] = {qbytes, kvbytes, kvbytes, qbytes, lbytes, qbytes};
+    void* out[4] = {dq, dk, dv, delta};
+    const uint64_t out_n[4] = {qbytes, kvbytes, kvbytes, lbytes};
+    for (int a = 0; a < 4; ++a) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(out[a], out_n[a], in[i], in_n[i]))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta must not overlap the inputs or each other");
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(out[a], out_n[a], out[b], out_n[b]))
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta must not overlap the inputs or each other");
+    }
+    // one workgroup per 4 rows (delta), per 128 query rows (dq), per 128 keys (dk, dv)
+    const uint64_t tiles = ((uint64_t)N + 127) / 128;
+    if ((qrows + 3) / 4 > 0x7fffffffULL || (uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.delta = delta;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.group = Hq / Hkv;
+    p.scale = scale;
+    p.xcd_map = 0;
+    const hipError_t err = fa::launch_bwd(p, d, dtype, causal, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +374,12 @@ int fa_softmax(const void* x, void* y, float* lse, long long rows, int cols, int
     return run_softmax(x, y, lse, rows, cols, dtype, algo, stream);
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int N, int d, int causal,
+           float scale, int dtype, void* stream)
+{
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int N, int d, int causal, float scale, int dtype, void* stream)
@@ -391,7 +468,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 3;
+    return 4;
 }
 
 }  // extern "C"

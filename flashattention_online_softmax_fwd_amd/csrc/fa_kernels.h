@@ -60,6 +60,27 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams& p, int d, int out_dtype, hipStream_t stream);   // FA_DTYPE_*
 
+// Backward pass (16-bit inputs): dq, dk, dv from q, k, v, o, do and the forward's lse.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;   // dO [B][Hq][N][d]
+    const float* lse;   // [B][Hq][N], natural log
+    float* delta;       // [B][Hq][N]: rowsum(dO * O), written by the first kernel
+    void* dq;           // [B][Hq][N][d]
+    void* dk;           // [B][Hkv][N][d]
+    void* dv;           // [B][Hkv][N][d]
+    int B, Hq, Hkv, N;
+    int group;          // Hq / Hkv
+    float scale;        // multiplies q.k
+    int xcd_map;        // set by the launchers
+};
+// Enqueues the three kernels (delta, dq, dk/dv) on the stream; d is 64 or 128,
+// dtype FA_DTYPE_BF16 or FA_DTYPE_F16.
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, int causal, hipStream_t stream);
+
 // Row softmax: y [rows][cols] = softmax of each row of x, lse [rows] (optional).
 struct SoftmaxParams {
     const void* x;

@@ -9,7 +9,8 @@ Recipe: ``numpy.random.default_rng(seed)`` draws Q, K and V (in that order) as
 float32 standard normals of shape [B, Hq, N, d], [B, Hkv, N, d], [B, Hkv, N, d];
 Q is then multiplied by ``q_mult``; bf16 workloads round to bfloat16 with
 round-to-nearest-even (``torch.Tensor.to``), fp16 ones likewise.  The oracle reads the rounded
-values upcast exactly to float64.
+values upcast exactly to float64.  The backward's upstream gradient dO is drawn the same
+way, from its own generator seeded with the workload's seed + 50000.
 """
 from __future__ import annotations
 
@@ -76,6 +77,16 @@ WORKLOADS = {
 }
 
 BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
+
+# Backward workloads: the shapes of the bench forward, of the GQA forward and of the
+# d = 64 forward, with their own seeds (dO drawn like Q, K and V).
+BWD_WORKLOADS = {
+    "b1_bf16_bwd_n4096_d128_causal": Workload("b1_bf16_bwd_n4096_d128_causal", 2, 32, 32, 4096, 128, "bf16",
+                                              True, seed=1301),
+    "b2_bf16_bwd_gqa_n8192_d128_causal": Workload("b2_bf16_bwd_gqa_n8192_d128_causal", 1, 32, 8, 8192, 128,
+                                                  "bf16", True, seed=1302),
+    "b3_bf16_bwd_n2048_d64": Workload("b3_bf16_bwd_n2048_d64", 4, 16, 16, 2048, 64, "bf16", False, seed=1303),
+}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -203,6 +214,25 @@ def make_qkv(B, Hq, Hkv, N, d, dtype="bf16", seed=0, q_mult=1.0, Nk=None):
 
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.q_mult)
+
+
+def make_dout(B, Hq, N, d, dtype="bf16", seed=0):
+    """Seeded upstream gradient dO [B, Hq, N, d]: float32 standard normals rounded to the dtype."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
+    return torch.from_numpy(g).to(torch_dtype(dtype))
+
+
+def bwd_workload_inputs(w: Workload):
+    """(q, k, v, dO) of a backward workload; dO is drawn with seed + 50000."""
+    q, k, v = workload_inputs(w)
+    return q, k, v, make_dout(w.B, w.Hq, w.N, w.d, w.dtype, w.seed + 50000)
+
+
+def bwd_flops(w: Workload) -> float:
+    """The five products of the backward (S, dP, dV, dK, dQ), 2*N^2*d flops each per
+    head, halved when causal: 2.5 times the forward's count."""
+    return 2.5 * w.flops
 
 
 def sample_rows(w: Workload, count: int, seed: int | None = None):

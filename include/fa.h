@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of libfa, the MI355X (gfx950) FlashAttention forward library.
+ * fa.h -- C ABI of libfa, the MI355X (gfx950) FlashAttention library: the forward,
+ * its split-KV form, the row softmax and the backward.
  *
  * The one operation is exact scaled-dot-product attention,
  *
@@ -195,13 +196,43 @@ enum {
 int fa_softmax(const void* x, void* y, float* lse, long long rows, int cols, int dtype, int algo,
                void* stream);
 
+/*
+ * fa_bwd: gradients of the square problem of fa_fwd with respect to q, k and v,
+ * given the upstream gradient dout of o.  The forward's N x N weights are not
+ * kept: the backward recomputes them from q, k and the forward's lse (the
+ * paweldubiel.com FlashAttention note, "Mechanism and details", and the
+ * spicyshark.co lesson, "Further reading": training recomputes in the backward
+ * what the forward did not store).  With P = softmax(scale q K^T) (masked keys 0):
+ *     D  = rowsum(dout * o),   dP = dout v^T,   dS = P * (dP - D)
+ *     dq = scale dS k,         dk = scale dS^T q,   dv = P^T dout
+ * dk and dv of a K/V head sum over the Hq/Hkv query heads that read it.
+ *
+ *   q, k, v, o, lse   the forward's inputs and outputs (o and lse as fa_fwd wrote
+ *             them for the same q, k, v, causal and scale), read only
+ *   dout      [B][Hq][N][d] in dtype, read only
+ *   dq        [B][Hq][N][d] in dtype, written
+ *   dk, dv    [B][Hkv][N][d] in dtype, written
+ *   delta     [B][Hq][N] float32, written: D of every row (workspace of the call,
+ *             returned because it is useful)
+ *   dtype     FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32: FA_ERR_UNSUPPORTED);
+ *             products in the 16-bit type with fp32 accumulation, P and dS
+ *             rounded to the 16-bit type as the MFMA operands they are
+ *   B, N, Hq, Hkv, d, causal, scale, stream: as for fa_fwd
+ * dq, dk, dv and delta must not overlap each other or any input.  Ownership,
+ * alignment and error rules as for fa_fwd.  Every output element is accumulated
+ * in a fixed order: results are bitwise reproducible (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+           int N, int d, int causal, float scale, int dtype, void* stream);
+
 /* Static text for a return code. */
 const char* fa_error_string(int code);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

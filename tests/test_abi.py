@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
                           "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
-                          "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax"}
+                          "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax", "fa_bwd"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -64,7 +64,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -202,3 +202,30 @@ def test_softmax_rejects_bad_arguments(lib, args, code):
 def test_softmax_empty_matrix_is_ok(lib):
     assert lib.fa_softmax(0, 0, 0, 0, 64, 0, 0, None) == 0
     assert lib.fa_softmax(0, 0, 0, 0, 0, 1, 1, None) == 0
+
+
+def call_bwd(lib, q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000, do=P + 0x500000,
+             dq=P + 0x600000, dk=P + 0x700000, dv=P + 0x800000, delta=P + 0x900000, B=1, Hq=2, Hkv=1, N=300,
+             d=64, causal=1, scale=0.125, dtype=1, stream=None):
+    return lib.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(do=0), 1), (dict(delta=0), 1), (dict(dv=P + 0x800008), 1),
+    (dict(B=-1), 1), (dict(N=-1), 1), (dict(Hq=3, Hkv=2), 1), (dict(Hkv=0), 1), (dict(causal=2), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=3e38), 1),
+    (dict(dtype=0), 2), (dict(dtype=5), 1), (dict(d=80), 2),
+    (dict(dq=P + 0x500000), 1),                           # dq overlaps dO
+    (dict(dk=P + 0x600100), 1),                           # dk overlaps dq
+    (dict(delta=P + 0x300000), 1),                        # delta overlaps o
+    (dict(dv=P + 0x400000), 1),                           # dv overlaps lse
+])
+def test_bwd_rejects_bad_arguments_before_any_hip_call(lib, kw, code):
+    assert call_bwd(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_bwd_empty_problems(lib):
+    z = dict(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0)
+    assert call_bwd(lib, B=0, **z) == 0
+    assert call_bwd(lib, N=0, **z) == 0
