@@ -364,7 +364,7 @@ def run_softmax_workload(name, steps, warmup):
 
 def run_bwd_workload(name, steps, warmup):
     """Backward pass (dq, dk, dv from q, k, v, o, lse and dO); one step is one fa_bwd
-    call, its three kernels (delta, dq, dk/dv) back to back on one stream.
+    call, its two kernels (dq with D = rowsum(dO o), then dk/dv) back to back on one stream.
 
     ``value`` counts the five products of the backward (S, dP, dV, dK, dQ: 2.5 times
     the forward's flops) per step over the timed wall time.  The kernels recompute S
@@ -427,7 +427,7 @@ def run_bwd_workload(name, steps, warmup):
                    "causal": w.causal, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_for(w.name, "bwd"),
-                     "kernel": "fa_bwd (fa::bwd_delta_kernel + fa::bwd_dq_kernel + fa::bwd_dkdv_kernel)",
+                     "kernel": "fa_bwd (fa::bwd_dq_kernel + fa::bwd_dkdv_kernel)",
                      "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops},
     }
 

@@ -9,10 +9,10 @@
 //     D  = rowsum(dO * O)
 //     dP = dO v^T,  dS = P * (dP - D)
 //     dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
-// the exact gradient of O = softmax(scale Q K^T) V.  Three kernels, in stream order:
-//   delta   one wave per row: D into the caller's delta buffer;
-//   dq      one workgroup per 128 query rows (4 waves x 32), looping over key tiles
-//           as the forward does: S^T = K Q^T and dP^T = V dO^T, dS^T, then
+// the exact gradient of O = softmax(scale Q K^T) V.  Two kernels, in stream order:
+//   dq      one workgroup per 128 query rows (4 waves x 32): D of each row from its O
+//           and dO (written to the caller's delta buffer), then a loop over key tiles
+//           as the forward's: S^T = K Q^T and dP^T = V dO^T, dS^T, then
 //           dQ^T += K^T dS^T (K^T from transposed LDS reads);
 //   dkdv    one workgroup per 128 keys (4 waves x 32), looping over 32-query tiles
 //           of every query head that reads this K/V head: S = Q K^T and dP = dO V^T,
@@ -31,25 +31,6 @@ namespace fa {
 namespace bwd {
 constexpr float kLog2e = 1.4426950408889634f;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-}
-
-// D = rowsum(dO * O) in fp32, one wave per row.
-template <typename E, int D>
-__global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdParams p)
-{
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const long long rows = (long long)p.B * p.Hq * p.N;
-    if (row >= rows) return;
-    const E* o = (const E*)p.o + row * D + PER * lane;
-    const E* g = (const E*)p.dout + row * D + PER * lane;
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (lane == 0) p.delta[row] = acc;
 }
 
 // dQ: per query tile of 128 rows, over the key tiles the rows see.
@@ -80,11 +61,9 @@ bwd_dq_kernel(const BwdParams p)
     const int bid = blockIdx.x;
     int bh, qt;
     if (p.xcd_map) {
-        const int xcd = bid & 7;
-        const int k = bid >> 3;
-        bh = xcd * (bhc >> 3) + k / nqt;
-        const int t = k % nqt;
-        qt = CAUSAL ? nqt - 1 - t : t;
+        int t;
+        xcd_order(bid, bhc, nqt, bh, t);
+        qt = CAUSAL ? nqt - 1 - t : t;   // longest first
     } else {
         bh = bid % bhc;
         qt = CAUSAL ? nqt - 1 - bid / bhc : bid / bhc;
@@ -122,7 +101,19 @@ bwd_dq_kernel(const BwdParams p)
     }
     const float c = p.scale * bwd::kLog2e;
     const float lse2 = row_ok ? p.lse[qrow] * bwd::kLog2e : 0.f;
-    const float dlt = row_ok ? p.delta[qrow] : 0.f;
+    // D = rowsum(dO * O) of this lane's row: each lane half takes its 64 (or 32) dims,
+    // then one swap.  Written for the dK/dV kernel, which runs next on the stream.
+    float dpart = 0.f;
+    if (row_ok) {
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const ex8 ov = __builtin_bit_cast(ex8, *(const u32x4*)((const E*)p.o + qrow * D + 16 * kk + 8 * hi));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)ov[e], (float)gf[kk][e], dpart);
+        }
+    }
+    const float dlt = lane_half_sum(dpart);
+    if (row_ok && hi == 0) p.delta[qrow] = dlt;
 
     const int kx = swz<D>(l32);
     int koff[DK];
@@ -288,10 +279,7 @@ bwd_dkdv_kernel(const BwdParams p)
     const int bid = blockIdx.x;
     int bkv, kt;
     if (p.xcd_map) {
-        const int xcd = bid & 7;
-        const int k = bid >> 3;
-        bkv = xcd * (bkvc >> 3) + k / nkt;
-        kt = k % nkt;                       // causal: early key tiles see the most queries
+        xcd_order(bid, bkvc, nkt, bkv, kt);   // causal: early key tiles see the most queries
     } else {
         bkv = bid % bkvc;
         kt = bid / bkvc;
@@ -505,7 +493,6 @@ bwd_dkdv_kernel(const BwdParams p)
 }
 
 #define FA_BWD_INSTANTIATE(E, D)                                                   \
-    template __global__ void bwd_delta_kernel<E, D>(const BwdParams);             \
     template __global__ void bwd_dq_kernel<E, D, false>(const BwdParams);         \
     template __global__ void bwd_dq_kernel<E, D, true>(const BwdParams);          \
     template __global__ void bwd_dkdv_kernel<E, D, false>(const BwdParams);       \
@@ -521,14 +508,10 @@ template <typename E, int D>
 hipError_t launch_bwd_t(const BwdParams& p0, int causal, hipStream_t stream)
 {
     BwdParams p = p0;
-    const long long rows = (long long)p.B * p.Hq * p.N;
     void* kargs[] = {&p};
-    hipError_t err = hipLaunchKernel((const void*)&bwd_delta_kernel<E, D>, dim3((unsigned)((rows + 3) / 4)),
-                                     dim3(256), kargs, 0, stream);
-    if (err != hipSuccess) return err;
     const long long nqt = (p.N + 127) / 128;
     p.xcd_map = ((long long)p.B * p.Hq) % 8 == 0 ? 1 : 0;
-    err = hipLaunchKernel(causal ? (const void*)&bwd_dq_kernel<E, D, true> : (const void*)&bwd_dq_kernel<E, D, false>,
+    hipError_t err = hipLaunchKernel(causal ? (const void*)&bwd_dq_kernel<E, D, true> : (const void*)&bwd_dq_kernel<E, D, false>,
                           dim3((unsigned)((long long)p.B * p.Hq * nqt)), dim3(256), kargs, 0, stream);
     if (err != hipSuccess) return err;
     const long long nkt = (p.N + 127) / 128;

@@ -93,13 +93,9 @@ fwd16_kernel(const FwdParams p)
     const int bid = blockIdx.x;
     int u, qt;
     if (p.xcd_map) {
-        // Blocks go to the 8 XCDs round-robin.  Give each XCD a contiguous run of heads
-        // (so its L2 holds few K/V heads at a time), each head's tiles longest first.
-        const int xcd = bid & 7;
-        const int k = bid >> 3;
-        u = xcd * (units >> 3) + k / nqt;
-        const int t = k % nqt;
-        qt = CAUSAL ? nqt - 1 - t : t;
+        int t;
+        xcd_order(bid, units, nqt, u, t);
+        qt = CAUSAL ? nqt - 1 - t : t;   // longest first
     } else {
         u = bid % units;
         qt = CAUSAL ? nqt - 1 - bid / units : bid / units;

@@ -337,9 +337,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             if (overlaps(out[a], out_n[a], out[b], out_n[b]))
                 return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta must not overlap the inputs or each other");
     }
-    // one workgroup per 4 rows (delta), per 128 query rows (dq), per 128 keys (dk, dv)
+    // one workgroup per 128 query rows (dq) and per 128 keys (dk, dv)
     const uint64_t tiles = ((uint64_t)N + 127) / 128;
-    if ((qrows + 3) / 4 > 0x7fffffffULL || (uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL)
+    if ((uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
 
     fa::BwdParams p;

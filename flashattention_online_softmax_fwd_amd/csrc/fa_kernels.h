@@ -68,7 +68,7 @@ struct BwdParams {
     const void* o;
     const void* dout;   // dO [B][Hq][N][d]
     const float* lse;   // [B][Hq][N], natural log
-    float* delta;       // [B][Hq][N]: rowsum(dO * O), written by the first kernel
+    float* delta;       // [B][Hq][N]: rowsum(dO * O), written by the dq kernel
     void* dq;           // [B][Hq][N][d]
     void* dk;           // [B][Hkv][N][d]
     void* dv;           // [B][Hkv][N][d]
@@ -77,7 +77,7 @@ struct BwdParams {
     float scale;        // multiplies q.k
     int xcd_map;        // set by the launchers
 };
-// Enqueues the three kernels (delta, dq, dk/dv) on the stream; d is 64 or 128,
+// Enqueues the two kernels (dq with D, then dk/dv) on the stream; d is 64 or 128,
 // dtype FA_DTYPE_BF16 or FA_DTYPE_F16.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, int causal, hipStream_t stream);
 

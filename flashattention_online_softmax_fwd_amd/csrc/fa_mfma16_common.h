@@ -86,6 +86,30 @@ __device__ __forceinline__ void tile_barrier()
     __syncthreads();
 }
 
+// Workgroup order over the 8 XCDs, which receive blocks round-robin (block b runs on
+// XCD b % 8).  Each XCD gets a contiguous run of the units (heads) so that its L2 holds
+// few of them at a time, and walks them two at a time, the tiles of the pair
+// interleaved: (u0, t0), (u1, t0), (u0, t1), (u1, t1), ...  Under causal masking the
+// callers map t = 0 to the longest tile, so all long tiles of a pair start before its
+// short ones and the short tiles of the last pair fill the tail of the grid.  Units
+// per XCD (units / 8, units a multiple of 8) odd: one unit at a time.
+__device__ __forceinline__ void xcd_order(int bid, int units, int ntiles, int& u, int& t)
+{
+    const int xcd = bid & 7;
+    const int k = bid >> 3;
+    const int per = units >> 3;
+    if ((per & 1) == 0) {
+        const int pair = k / (2 * ntiles);
+        const int r = k - pair * 2 * ntiles;
+        u = xcd * per + 2 * pair + (r & 1);
+        t = r >> 1;
+    } else {
+        const int q = k / ntiles;
+        u = xcd * per + q;
+        t = k - q * ntiles;
+    }
+}
+
 template <bool V>
 struct Flag {
     static constexpr bool value = V;
