@@ -1,7 +1,7 @@
 """Static checks on the gfx950 code the kernels compile to (CPU only: hipcc here).
 
-The 16-bit (bf16 and fp16) kernel stages K/V tiles with loads that write LDS directly
-(buffer_load ... lds).  Those loads count in vmcnt, and a workgroup barrier does
+The 16-bit (bf16 and fp16) forward and backward kernels stage tiles with loads that
+write LDS directly (buffer_load ... lds).  Those loads count in vmcnt, and a workgroup barrier does
 not by itself wait for them: every s_barrier must therefore follow an s_waitcnt
 that includes vmcnt(0), or a wave could pass the barrier while its part of the
 next tile is still landing and other waves would read stale data.
@@ -18,20 +18,29 @@ CSRC = os.path.join(ROOT, "flashattention_online_softmax_fwd_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 
-@pytest.fixture(scope="module")
-def bf16_asm(tmp_path_factory):
+def compile_asm(tmp_path_factory, source):
     if not HIPCC:
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("isa") / "bf16.s")
+    out = str(tmp_path_factory.mktemp("isa") / (source + ".s"))
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
                     "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
-                    "--offload-device-only", "-S", os.path.join(CSRC, "fa_fwd_mfma16.hip"), "-o", out],
+                    "--offload-device-only", "-S", os.path.join(CSRC, source), "-o", out],
                    check=True, capture_output=True)
     return open(out).read()
 
 
-def kernels(asm):
-    for name in re.findall(r"^(_ZN2fa12fwd16_kernel\S+):", asm, re.M):
+@pytest.fixture(scope="module")
+def bf16_asm(tmp_path_factory):
+    return compile_asm(tmp_path_factory, "fa_fwd_mfma16.hip")
+
+
+@pytest.fixture(scope="module")
+def bwd_asm(tmp_path_factory):
+    return compile_asm(tmp_path_factory, "fa_bwd_mfma16.hip")
+
+
+def kernels(asm, pattern=r"_ZN2fa12fwd16_kernel"):
+    for name in re.findall(r"^(%s\S+):" % pattern, asm, re.M):
         i = asm.index(name + ":")
         j = asm.index(".Lfunc_end", i)
         body = [l.strip() for l in asm[i:j].splitlines()]
@@ -56,3 +65,16 @@ def test_no_packed_fp32_and_no_scratch(bf16_asm):
     for name, ins in kernels(bf16_asm):
         if "Li128ELi64E" in name:
             assert not any(x.startswith("scratch_") for x in ins), name
+
+
+def test_backward_barriers_wait_for_lds_dma_and_nothing_spills(bwd_asm):
+    found = 0
+    for name, ins in kernels(bwd_asm, r"_ZN2fa1[35]bwd_d\w+_kernel"):
+        found += 1
+        assert any(x.startswith("buffer_load_dword") and x.endswith("lds") for x in ins), name
+        for n, x in enumerate(ins):
+            if x.startswith("s_barrier"):
+                assert ins[n - 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[n - 1], (name, n, ins[n - 1])
+        assert not any(x.startswith(("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")) for x in ins), name
+        assert not any(x.startswith("scratch_") for x in ins), name
+    assert found == 16      # dq and dk/dv, bf16 and fp16, d 64 and 128, causal or not
