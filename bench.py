@@ -363,8 +363,9 @@ def run_softmax_workload(name, steps, warmup):
 
 
 def run_bwd_workload(name, steps, warmup):
-    """Backward pass (dq, dk, dv from q, k, v, o, lse and dO); one step is one fa_bwd
-    call, its two kernels (dq with D = rowsum(dO o), then dk/dv) back to back on one stream.
+    """Backward pass (dq, dk, dv from q, k, v, o, lse and dO); one step is one fa_bwd_split
+    call with fa_bwd_num_splits splits: its kernels (dq with D = rowsum(dO o), dk/dv, and
+    the sum of the dk/dv partials when there are several splits) back to back on one stream.
 
     ``value`` counts the five products of the backward (S, dP, dV, dK, dQ: 2.5 times
     the forward's flops) per step over the timed wall time.  The kernels recompute S
@@ -386,13 +387,16 @@ def run_bwd_workload(name, steps, warmup):
     o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    S = _lib.fa_bwd_num_splits(w.B, w.Hq, w.Hkv, w.N)
+    part = torch.empty((2, S) + tuple(k.shape), dtype=torch.float32, device=dev) if S > 1 else None
     dt = {"bf16": _lib.FA_DTYPE_BF16, "f16": _lib.FA_DTYPE_F16}[w.dtype]
     stream = torch.cuda.current_stream()
 
     def call():
-        rc = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), w.B, w.Hq, w.Hkv, w.N,
-                         w.d, int(w.causal), w.softmax_scale, dt, stream.cuda_stream)
+        rc = _lib.fa_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                               part.data_ptr() if part is not None else None, S, w.B, w.Hq, w.Hkv, w.N, w.d,
+                               int(w.causal), w.softmax_scale, dt, stream.cuda_stream)
         assert rc == 0, _lib.fa_last_error()
 
     for _ in range(warmup):
@@ -424,10 +428,10 @@ def run_bwd_workload(name, steps, warmup):
         "dtype": w.dtype,
         "data": "synthetic (seeded normal Q/K/V/dO, numpy default_rng(%d), dO seed + 50000)" % w.seed,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "flops_per_step": flops},
+                   "causal": w.causal, "dkdv_splits": S, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_for(w.name, "bwd"),
-                     "kernel": "fa_bwd (fa::bwd_dq_kernel + fa::bwd_dkdv_kernel)",
+                     "kernel": "fa_bwd_split (fa::bwd_dq_kernel + fa::bwd_dkdv_kernel [+ fa::bwd_reduce_kernel])",
                      "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops},
     }
 

@@ -20,11 +20,11 @@ import torch
 from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FA_ERR_HIP, FA_ERR_INVALID_ARG,
                    FA_ERR_UNSUPPORTED, FA_OK, FA_SOFTMAX_ONLINE, FA_SOFTMAX_SAFE, LibraryNotBuilt,
-                   fa_abi_version, fa_bwd, fa_error_string, fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error,
+                   fa_abi_version, fa_bwd, fa_bwd_num_splits, fa_bwd_split, fa_error_string, fa_fwd, fa_fwd_splitkv, fa_fwd_tiled, fa_last_error,
                    fa_merge, fa_softmax, fa_split_chunk, fa_splitkv_num_splits, fa_tile_shapes)
 
 __all__ = ["forward", "forward_splitkv", "merge", "attention_kv", "softmax", "backward", "attention",
-           "fa_fwd", "fa_fwd_tiled", "fa_bwd",
+           "fa_fwd", "fa_fwd_tiled", "fa_bwd", "fa_bwd_split", "fa_bwd_num_splits",
            "fa_fwd_splitkv", "fa_merge", "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax",
            "FA_SOFTMAX_ONLINE", "FA_SOFTMAX_SAFE",
            "fa_tile_shapes", "fa_error_string",
@@ -244,14 +244,18 @@ def softmax(x, algo="online", out=None, lse=None):
     return out, lse
 
 
-def backward(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None, delta=None):
+def backward(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None, delta=None,
+             num_splits=None):
     """Gradients of the square attention forward: returns (dq, dk, dv, delta).
 
     q, o, do [B, Hq, N, d] and k, v [B, Hkv, N, d] bfloat16 or float16 CUDA tensors,
     contiguous; o and lse [B, Hq, N] float32 as ``forward`` returned them for the same
     q, k, v, causal and scale.  delta [B, Hq, N] float32 is rowsum(do * o).  dk and
     dv of a K/V head sum over the query heads that read it.  The gradient buffers
-    may be given to write into existing tensors.  Runs on torch's current stream.
+    may be given to write into existing tensors.  ``num_splits`` shares each key
+    tile's dK/dV work over that many workgroups through an fp32 workspace this
+    function allocates (default: ``fa_bwd_num_splits``; 1 needs no workspace).  Runs
+    on torch's current stream.
     """
     lib = _lib.load()
     _check_inputs(q, k, v)
@@ -282,11 +286,17 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv
     elif (delta.shape != (B, Hq, N) or delta.dtype != torch.float32 or delta.device != q.device
           or not delta.is_contiguous()):
         raise ValueError("delta must be a contiguous float32 tensor [B, Hq, N] on q's device")
+    if num_splits is None:
+        num_splits = max(1, fa_bwd_num_splits(max(B, 1), Hq, Hkv, max(N, 1)))
+    part = None
+    if num_splits > 1 and B * N > 0:
+        part = torch.empty((2, num_splits) + tuple(k.shape), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, N, d,
-                        int(bool(causal)), float(scale), _DTYPES[q.dtype], stream)
+        rc = lib.fa_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                              part.data_ptr() if part is not None else None, int(num_splits), B, Hq, Hkv, N, d,
+                              int(bool(causal)), float(scale), _DTYPES[q.dtype], stream)
     if rc != FA_OK:
         _raise(rc)
     return dq, dk, dv, delta

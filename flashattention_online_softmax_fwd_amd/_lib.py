@@ -41,6 +41,8 @@ SIGNATURES = {
     "fa_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_softmax": (_I, [_P, _P, _P, ctypes.c_longlong, _I, _I, _I, _P]),
     "fa_bwd": (_I, [_P] * 10 + [_I] * 6 + [ctypes.c_float, _I, _P]),
+    "fa_bwd_split": (_I, [_P] * 11 + [_I] * 7 + [ctypes.c_float, _I, _P]),
+    "fa_bwd_num_splits": (_I, [_I, _I, _I, _I]),
     "fa_error_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (_I, []),
@@ -104,6 +106,16 @@ def fa_softmax(x, y, lse, rows, cols, dtype, algo, stream):
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype, stream):
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype,
                          stream)
+
+
+def fa_bwd_split(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits, B, Hq, Hkv, N, d, causal,
+                 scale, dtype, stream):
+    return load().fa_bwd_split(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits, B, Hq, Hkv, N, d,
+                               causal, scale, dtype, stream)
+
+
+def fa_bwd_num_splits(B, Hq, Hkv, N):
+    return load().fa_bwd_num_splits(B, Hq, Hkv, N)
 
 
 def fa_tile_shapes(dtype, d):

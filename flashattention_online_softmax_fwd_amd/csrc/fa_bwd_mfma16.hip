@@ -18,6 +18,9 @@
 //           of every query head that reads this K/V head: S = Q K^T and dP = dO V^T,
 //           so one key per lane and the rounded P and dS are directly the B operands
 //           of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T from transposed reads).
+//           When the grid is small, each key tile's query tiles are shared out over S
+//           workgroups that write fp32 partial sums; a last kernel adds the S partials
+//           of every element in split order and rounds them.
 // Every output element is accumulated by one wave in a fixed order: no atomics,
 // results reproducible bit for bit.  LDS tiles use the forward's layout (16-byte
 // chunks XOR-swizzled per row, filled by buffer_load ... lds).
@@ -276,14 +279,17 @@ bwd_dkdv_kernel(const BwdParams p)
     const int Gq = p.group;
     const int bkvc = p.B * p.Hkv;
     const int nkt = (N + BK - 1) / BK;
+    const int S = p.splits;
     const int bid = blockIdx.x;
-    int bkv, kt;
+    int bkv, kts;   // kts = kt * S + split: the splits of one key tile are adjacent
     if (p.xcd_map) {
-        xcd_order(bid, bkvc, nkt, bkv, kt);   // causal: early key tiles see the most queries
+        xcd_order(bid, bkvc, nkt * S, bkv, kts);   // causal: early key tiles see the most queries
     } else {
         bkv = bid % bkvc;
-        kt = bid / bkvc;
+        kts = bid / bkvc;
     }
+    const int kt = kts / S;
+    const int split = kts - kt * S;
     const int b = bkv / p.Hkv;
     const int hk = bkv - b * p.Hkv;
     const int k0 = kt * BK;
@@ -340,7 +346,11 @@ bwd_dkdv_kernel(const BwdParams p)
     const int nq = (N + BQ - 1) / BQ;
     const int qi0 = CAUSAL ? k0 / BQ : 0;
     const int per_head = nq - qi0;
-    const int ntiles = Gq * per_head;
+    // With S splits, split s takes a contiguous share of the G * per_head tiles.
+    const int all_tiles = Gq * per_head;
+    const int share = (all_tiles + S - 1) / S;
+    const int t_lo = min(all_tiles, split * share);
+    const int t_hi = min(all_tiles, t_lo + share);
 
     // V rows of this key tile into LDS once.
     {
@@ -394,7 +404,7 @@ bwd_dkdv_kernel(const BwdParams p)
         const float* lb = P == 0 ? ls_lds0 : ls_lds1;
         const float* db = P == 0 ? dl_lds0 : dl_lds1;
         tile_barrier();                                   // tile t (and V) landed; buffers 1-P free
-        if (t + 1 < ntiles) {
+        if (t + 1 < t_hi) {
             if constexpr (P == 0) issue(t + 1, q_lds1, g_lds1, ls_lds1, dl_lds1);
             else issue(t + 1, q_lds0, g_lds0, ls_lds0, dl_lds0);
         }
@@ -466,13 +476,36 @@ bwd_dkdv_kernel(const BwdParams p)
             }
     };
 
-    if (ntiles > 0) issue(0, q_lds0, g_lds0, ls_lds0, dl_lds0);
-    for (int t = 0; t < ntiles; t += 2) {
+    if (t_lo < t_hi) issue(t_lo, q_lds0, g_lds0, ls_lds0, dl_lds0);
+    for (int t = t_lo; t < t_hi; t += 2) {
         iter(t, Int<0>{});
-        if (t + 1 < ntiles) iter(t + 1, Int<1>{});
+        if (t + 1 < t_hi) iter(t + 1, Int<1>{});
     }
     tile_barrier();   // the V load above, when no tile was processed
 
+    if (S > 1) {   // fp32 partial sums, added up in split order by the reduce kernel
+        if (my_k < N) {
+            const size_t plane = (size_t)S * bkvc * N * D;
+            float* pk = p.dkv_part + ((size_t)split * bkvc * N + krow) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float4 wk, wv;
+                    wk.x = dk[dt][4 * g] * p.scale;
+                    wk.y = dk[dt][4 * g + 1] * p.scale;
+                    wk.z = dk[dt][4 * g + 2] * p.scale;
+                    wk.w = dk[dt][4 * g + 3] * p.scale;
+                    wv.x = dv[dt][4 * g];
+                    wv.y = dv[dt][4 * g + 1];
+                    wv.z = dv[dt][4 * g + 2];
+                    wv.w = dv[dt][4 * g + 3];
+                    *(float4*)(pk + 32 * dt + 8 * g + 4 * hi) = wk;
+                    *(float4*)(pk + plane + 32 * dt + 8 * g + 4 * hi) = wv;
+                }
+        }
+        return;
+    }
     if (my_k < N) {
         E* dkr = (E*)p.dk + krow * D;
         E* dvr = (E*)p.dv + krow * D;
@@ -492,11 +525,41 @@ bwd_dkdv_kernel(const BwdParams p)
     }
 }
 
+// dK and dV from S fp32 partials: out = sum over s of part[s], in split order.
+// part is [2][S][rows][D] (dK planes, then dV planes); one thread per 8 elements.
+template <typename E, int D>
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdParams p)
+{
+    typedef typename Elem<E>::x8 ex8;
+    const long long rows = (long long)p.B * p.Hkv * p.N;
+    const long long per_plane = rows * D / 8;                 // 8-element groups in dK (or dV)
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= 2 * per_plane) return;
+    const int which = i >= per_plane ? 1 : 0;                 // 0: dK, 1: dV
+    const long long e0 = (i - which * per_plane) * 8;
+    const size_t split_stride = (size_t)rows * D;
+    const float* src = p.dkv_part + (size_t)which * p.splits * split_stride + e0;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int sp = 0; sp < p.splits; ++sp) {
+        const float4 a = *(const float4*)(src + sp * split_stride);
+        const float4 b = *(const float4*)(src + sp * split_stride + 4);
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    ex8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (E)acc[e];
+    *(ex8*)((E*)(which ? p.dv : p.dk) + e0) = w;
+}
+
 #define FA_BWD_INSTANTIATE(E, D)                                                   \
     template __global__ void bwd_dq_kernel<E, D, false>(const BwdParams);         \
     template __global__ void bwd_dq_kernel<E, D, true>(const BwdParams);          \
     template __global__ void bwd_dkdv_kernel<E, D, false>(const BwdParams);       \
-    template __global__ void bwd_dkdv_kernel<E, D, true>(const BwdParams);
+    template __global__ void bwd_dkdv_kernel<E, D, true>(const BwdParams);       \
+    template __global__ void bwd_reduce_kernel<E, D>(const BwdParams);
 FA_BWD_INSTANTIATE(__bf16, 128)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(_Float16, 128)
@@ -516,8 +579,12 @@ hipError_t launch_bwd_t(const BwdParams& p0, int causal, hipStream_t stream)
     if (err != hipSuccess) return err;
     const long long nkt = (p.N + 127) / 128;
     p.xcd_map = ((long long)p.B * p.Hkv) % 8 == 0 ? 1 : 0;
-    return hipLaunchKernel(causal ? (const void*)&bwd_dkdv_kernel<E, D, true> : (const void*)&bwd_dkdv_kernel<E, D, false>,
-                           dim3((unsigned)((long long)p.B * p.Hkv * nkt)), dim3(256), kargs, 0, stream);
+    err = hipLaunchKernel(causal ? (const void*)&bwd_dkdv_kernel<E, D, true> : (const void*)&bwd_dkdv_kernel<E, D, false>,
+                          dim3((unsigned)((long long)p.B * p.Hkv * nkt * p.splits)), dim3(256), kargs, 0, stream);
+    if (err != hipSuccess || p.splits == 1) return err;
+    const long long groups = 2LL * p.B * p.Hkv * p.N * D / 8;
+    return hipLaunchKernel((const void*)&bwd_reduce_kernel<E, D>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
+                           kargs, 0, stream);
 }
 }  // namespace
 

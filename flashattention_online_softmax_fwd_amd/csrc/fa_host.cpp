@@ -19,6 +19,7 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr int kMaxSplits = 1024;
+constexpr int kMaxBwdSplits = 8;
 
 int fail(int code, const std::string& msg)
 {
@@ -295,8 +296,8 @@ int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, in
 }
 
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-            void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int N, int d, int causal,
-            float scale, int dtype, void* stream)
+            void* dq, void* dk, void* dv, float* delta, float* dkv_part, int num_splits, int B, int Hq, int Hkv,
+            int N, int d, int causal, float scale, int dtype, void* stream)
 {
     g_last_error.clear();
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
@@ -309,8 +310,13 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
     if (!std::isfinite((float)((double)scale * 1.4426950408889634)))
         return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    if (num_splits < 1 || num_splits > kMaxBwdSplits)
+        return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxBwdSplits));
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (B == 0 || N == 0) return FA_OK;
+    if (num_splits > 1 && !dkv_part) return fail(FA_ERR_INVALID_ARG, "dkv_part is required when num_splits > 1");
+    if (num_splits > 1 && reinterpret_cast<uintptr_t>(dkv_part) % 16 != 0)
+        return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
 
     const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
     for (const void* ptr : ptrs)
@@ -325,21 +331,27 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     if (qbytes >> 62 || kvbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
     if ((uint64_t)N * (uint64_t)d * 2 > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "one head of a tensor exceeds 2 GiB");
+    const uint64_t kvelems = kvbytes / 2;
+    const uint64_t pbytes = num_splits > 1 ? 2ULL * num_splits * kvelems * 4 : 0;   // fp32 partials
+    if (pbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
     const void* in[6] = {q, k, v, o, lse, dout};
     const uint64_t in_n[6] = {qbytes, kvbytes, kvbytes, qbytes, lbytes, qbytes};
-    void* out[4] = {dq, dk, dv, delta};
-    const uint64_t out_n[4] = {qbytes, kvbytes, kvbytes, lbytes};
-    for (int a = 0; a < 4; ++a) {
+    void* out[5] = {dq, dk, dv, delta, dkv_part};
+    const uint64_t out_n[5] = {qbytes, kvbytes, kvbytes, lbytes, pbytes};
+    const int nout = num_splits > 1 ? 5 : 4;
+    for (int a = 0; a < nout; ++a) {
         for (int i = 0; i < 6; ++i)
             if (overlaps(out[a], out_n[a], in[i], in_n[i]))
-                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta must not overlap the inputs or each other");
-        for (int b = a + 1; b < 4; ++b)
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv, delta and dkv_part must not overlap the inputs or each other");
+        for (int b = a + 1; b < nout; ++b)
             if (overlaps(out[a], out_n[a], out[b], out_n[b]))
-                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv and delta must not overlap the inputs or each other");
+                return fail(FA_ERR_INVALID_ARG, "dq, dk, dv, delta and dkv_part must not overlap the inputs or each other");
     }
-    // one workgroup per 128 query rows (dq) and per 128 keys (dk, dv)
+    // one workgroup per 128 query rows (dq), per 128 keys and split (dk, dv), per 8 elements (reduce)
     const uint64_t tiles = ((uint64_t)N + 127) / 128;
-    if ((uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL)
+    if ((uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL ||
+        (uint64_t)B * (uint64_t)Hkv * tiles * (uint64_t)num_splits > 0x7fffffffULL ||
+        (2 * kvelems / 8 + 255) / 256 > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
 
     fa::BwdParams p;
@@ -360,6 +372,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     p.group = Hq / Hkv;
     p.scale = scale;
     p.xcd_map = 0;
+    p.splits = num_splits;
+    p.dkv_part = num_splits > 1 ? dkv_part : nullptr;
     const hipError_t err = fa::launch_bwd(p, d, dtype, causal, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;
@@ -378,7 +392,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int N, int d, int causal,
            float scale, int dtype, void* stream)
 {
-    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale, dtype, stream);
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, nullptr, 1, B, Hq, Hkv, N, d, causal, scale, dtype,
+                   stream);
+}
+
+int fa_bwd_split(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, float* delta, float* dkv_part, int num_splits, int B, int Hq,
+                 int Hkv, int N, int d, int causal, float scale, int dtype, void* stream)
+{
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits, B, Hq, Hkv, N, d, causal, scale,
+                   dtype, stream);
+}
+
+int fa_bwd_num_splits(int B, int Hq, int Hkv, int N)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1) return -1;
+    // About 1024 dK/dV workgroups (two rounds of the chip's 512 slots) let the longest
+    // key tiles of a causal problem start first and the short ones fill in behind them.
+    const int64_t base = (int64_t)B * Hkv * (((int64_t)N + 127) / 128);
+    int64_t s = (1024 + base - 1) / base;
+    if (s > kMaxBwdSplits) s = kMaxBwdSplits;
+    return (int)s;
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
@@ -468,7 +502,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 4;
+    return 5;
 }
 
 }  // extern "C"

@@ -76,8 +76,11 @@ struct BwdParams {
     int group;          // Hq / Hkv
     float scale;        // multiplies q.k
     int xcd_map;        // set by the launchers
+    int splits;         // workgroups sharing each key tile's query tiles (1: dk, dv written directly)
+    float* dkv_part;    // splits > 1: [2][splits][B][Hkv][N][d] fp32 partial dK, then dV
 };
-// Enqueues the two kernels (dq with D, then dk/dv) on the stream; d is 64 or 128,
+// Enqueues the kernels (dq with D, then dk/dv, then the reduce when splits > 1) on the
+// stream; d is 64 or 128,
 // dtype FA_DTYPE_BF16 or FA_DTYPE_F16.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, int causal, hipStream_t stream);
 

@@ -38,9 +38,9 @@
  *
  * Ownership: every buffer belongs to the caller and is device memory of the
  * device the stream belongs to.  The library never allocates, frees or keeps a
- * pointer past the call and takes no workspace.  q, k and v are only read; o and
- * lse must not overlap the inputs or each other.  Every pointer must be 16-byte
- * aligned.
+ * pointer past the call; the only workspace it takes is fa_bwd_split's dkv_part.
+ * q, k and v are only read; o and lse must not overlap the inputs or each other.
+ * Every pointer must be 16-byte aligned.
  *
  * Errors: a return value other than FA_OK means nothing was enqueued.  Argument
  * errors are found on the host before any HIP call.  FA_ERR_HIP reports a
@@ -226,13 +226,38 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
            int N, int d, int causal, float scale, int dtype, void* stream);
 
+/*
+ * fa_bwd_split: fa_bwd with the dK/dV work of each 128-key tile shared out over
+ * num_splits workgroups, for problems whose grid of key tiles is too small to fill
+ * the GPU evenly (e.g. one sequence of a GQA model with 8 K/V heads): split s takes
+ * a contiguous share of the key tile's (query head, 32-query tile) pairs.  Each
+ * split writes fp32 partial sums, which a last kernel adds in split order and rounds
+ * into dk and dv, so results stay bitwise reproducible (and may differ from
+ * fa_bwd's only by the rounding of that sum).
+ *
+ *   dkv_part    [2][num_splits][B][Hkv][N][d] float32 device workspace owned by the
+ *               caller (partial dK planes, then dV planes); contents on entry are
+ *               ignored; may be NULL when num_splits is 1; must not overlap any
+ *               other argument
+ *   num_splits  1..8; 1 is fa_bwd exactly; fa_bwd_num_splits suggests one
+ *   other arguments, ownership, alignment and errors: as for fa_bwd
+ */
+int fa_bwd_split(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta, float* dkv_part,
+                 int num_splits, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                 int dtype, void* stream);
+
+/* A split count for fa_bwd_split that gives about 1024 dK/dV workgroups (1 when the
+ * key tiles alone reach that, at most 8), or -1 for a bad size. */
+int fa_bwd_num_splits(int B, int Hq, int Hkv, int N);
+
 /* Static text for a return code. */
 const char* fa_error_string(int code);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

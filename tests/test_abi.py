@@ -31,7 +31,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
                           "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
-                          "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax", "fa_bwd"}
+                          "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax", "fa_bwd", "fa_bwd_split",
+                          "fa_bwd_num_splits"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -64,7 +65,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -229,3 +230,36 @@ def test_bwd_empty_problems(lib):
     z = dict(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0)
     assert call_bwd(lib, B=0, **z) == 0
     assert call_bwd(lib, N=0, **z) == 0
+
+
+def call_bwd_split(lib, part=P + 0xa00000, splits=2, **kw):
+    a = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000, do=P + 0x500000,
+             dq=P + 0x600000, dk=P + 0x700000, dv=P + 0x800000, delta=P + 0x900000, B=1, Hq=2, Hkv=1, N=300,
+             d=64, causal=1, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return lib.fa_bwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                            a["delta"], part, splits, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                            a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0), 1), (dict(splits=9), 1), (dict(part=0), 1), (dict(part=P + 0xa00008), 1),
+    (dict(part=P + 0x700000), 1),                         # workspace overlaps dk
+    (dict(part=P + 0x500000), 1),                         # workspace overlaps dO
+    (dict(dtype=0), 2), (dict(d=96), 2), (dict(Hq=3, Hkv=2), 1),
+])
+def test_bwd_split_rejects_bad_arguments(lib, kw, code):
+    assert call_bwd_split(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_bwd_split_needs_no_workspace_for_one_split_and_sizes(lib):
+    z = dict(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0)
+    assert call_bwd_split(lib, part=0, splits=4, B=0, **z) == 0
+    # one split takes no workspace: it reaches the pointer checks, not the workspace check
+    assert call_bwd_split(lib, part=0, splits=1, q=0) == 1 and b"null" in lib.fa_last_error()
+    # GQA 32/8 at N = 8192, one sequence: 512 key-tile workgroups, so two splits
+    assert lib.fa_bwd_num_splits(1, 32, 8, 8192) == 2
+    assert lib.fa_bwd_num_splits(2, 32, 32, 4096) == 1
+    assert lib.fa_bwd_num_splits(1, 1, 1, 128) == 8
+    assert lib.fa_bwd_num_splits(0, 1, 1, 1) == -1 and lib.fa_bwd_num_splits(1, 3, 2, 8) == -1

@@ -104,17 +104,17 @@ def check(g, r, mc, dtype, what):
                              % (what, int(bad.sum()), bad.size, i, g[i], r[i], bound[i]))
 
 
-def run_gpu(fa, q, k, v, do, causal, scale):
+def run_gpu(fa, q, k, v, do, causal, scale, num_splits=None):
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
-    dq, dk, dv, delta = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu(), delta.cpu()
 
 
-def compare(fa, oracle, q, k, v, do, causal, scale, dtype, what):
+def compare(fa, oracle, q, k, v, do, causal, scale, dtype, what, num_splits=None):
     print("backward", what, flush=True)
-    dq, dk, dv, delta = run_gpu(fa, q, k, v, do, causal, scale)
+    dq, dk, dv, delta = run_gpu(fa, q, k, v, do, causal, scale, num_splits)
     rq, rk, rv, rd = oracle.attention_backward(q, k, v, do, causal=causal, scale=scale)
     mq, mk, mv, md = magnitudes(q, k, v, do, causal, scale)
     check(dq.double().numpy(), rq, mq, dtype, what + " dq")
@@ -140,6 +140,31 @@ def test_matches_the_oracle(fa, oracle, shape, d, causal, dtype):
     q, k, v = fin.make_qkv(B, Hq, Hkv, N, d, dtype, seed)
     do = fin.make_dout(B, Hq, N, d, dtype, seed + 50000)
     compare(fa, oracle, q, k, v, do, causal, 1.0 / np.sqrt(d), dtype, "%s d%d causal%d %s" % (shape, d, causal, dtype))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 17), (1, 4, 2, 130), (2, 8, 2, 384), (1, 4, 1, 1000)])
+def test_split_dkdv_matches_the_oracle(fa, oracle, shape, splits):
+    """Each key tile's query tiles shared over 1-8 workgroups (some get none when a key
+    tile has fewer tiles than splits) with fp32 partials summed in split order."""
+    B, Hq, Hkv, N = shape
+    q, k, v = fin.make_qkv(B, Hq, Hkv, N, 128, "bf16", 900 + N)
+    do = fin.make_dout(B, Hq, N, 128, "bf16", 901 + N)
+    compare(fa, oracle, q, k, v, do, True, 1.0 / np.sqrt(128), "bf16", "%s split%d" % (shape, splits), splits)
+
+
+def test_split_dkdv_is_deterministic_and_matches_one_split(fa):
+    q, k, v = (t.cuda() for t in fin.make_qkv(1, 8, 2, 700, 64, "f16", 71))
+    do = fin.make_dout(1, 8, 700, 64, "f16", 72).cuda()
+    o, lse = fa.forward(q, k, v, causal=True)
+    one = fa.backward(q, k, v, o, lse, do, causal=True, num_splits=1)
+    a = fa.backward(q, k, v, o, lse, do, causal=True, num_splits=4)
+    b = fa.backward(q, k, v, o, lse, do, causal=True, num_splits=4)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    assert torch.equal(a[0], one[0]) and torch.equal(a[3], one[3])      # dq and D do not depend on the split
+    for x, y in zip(a[1:3], one[1:3]):                                    # dk, dv: fp32 sums regrouped
+        assert torch.allclose(x.float(), y.float(), rtol=2 ** -9, atol=1e-6)
 
 
 @pytest.mark.parametrize("scale", [1.0, -0.3, 0.0])
