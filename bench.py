@@ -182,6 +182,9 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
                    "flops_per_step": w.flops},
         "frac_of_peak": tflops / peak,
         "hbm_gbps": w.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9,
+        # for contrast only: one fp32 write of the N x N score table per head, which the
+        # tiled method never makes (the textbook path also reads it back at least once)
+        "textbook_score_bytes": 4 * w.B * w.Hq * w.N * w.N,
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
@@ -192,6 +195,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
             "kernel": "fa::fwd_f32_kernel" if w.dtype == "f32" else "fa::fwd16_kernel<%s>" % w.dtype,
             "avg_launch_ms": avg_launch_ms,
             "min_launch_ms": min(per_ms),
+            "median_launch_ms": sorted(per_ms)[len(per_ms) // 2],
             "algorithmic_flops_per_launch": w.flops,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
         },
