@@ -294,13 +294,15 @@ def run_kv_workload(name, steps, warmup):
 # Reads and writes per element of each row-softmax algorithm (spicyshark.co lesson, "The cost:
 # three passes" and "Why reading once matters").
 SOFTMAX_ACCESSES = {"online": (2, 1), "safe": (3, 1)}
+ROW_ON_CHIP_BYTES = 64 * 1024   # a row this long fits in one workgroup's share of a CU's 160 KB LDS
 
 
 def run_softmax_workload(name, steps, warmup):
     """Row softmax of a [rows, cols] matrix by both algorithms; one step is one launch.
 
     Each algorithm is priced against HBM with its own access count (the bytes it
-    must move if nothing stays on chip between its passes); ``value`` is the
+    must move when a row is too long to stay on chip between its passes; a row that
+    fits in one workgroup's LDS is priced at x once and y once); ``value`` is the
     online algorithm's effective rate, x read once plus y written once, over its
     wall time.
     """
@@ -337,6 +339,11 @@ def run_softmax_workload(name, steps, warmup):
         wall = time.perf_counter() - t0
         ms = sum(a.elapsed_time(b) for a, b in ev) / steps
         reads, writes = SOFTMAX_ACCESSES[algo]
+        # A row that fits in one workgroup's LDS could be read from HBM once whatever the
+        # algorithm, so only x once and y once are algorithmic; a longer row must be read
+        # from HBM as often as the algorithm passes over it.
+        if w.cols * w.esize <= ROW_ON_CHIP_BYTES:
+            reads, writes = 1, 1
         nbytes = (reads + writes) * w.rows * w.cols * w.esize + 4 * w.rows
         gbps = nbytes / (ms * 1e-3) / 1e9
         out[algo] = {"wall_s": wall, "ms": ms, "roofline": {
