@@ -78,14 +78,16 @@ WORKLOADS = {
 
 BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
 
-# Backward workloads: the shapes of the bench forward, of the GQA forward and of the
-# d = 64 forward, with their own seeds (dO drawn like Q, K and V).
+# Backward workloads: the shapes of the bench forward (bf16 and fp16), of the GQA forward
+# and of the d = 64 forward, with their own seeds (dO drawn like Q, K and V).
 BWD_WORKLOADS = {
     "b1_bf16_bwd_n4096_d128_causal": Workload("b1_bf16_bwd_n4096_d128_causal", 2, 32, 32, 4096, 128, "bf16",
                                               True, seed=1301),
     "b2_bf16_bwd_gqa_n8192_d128_causal": Workload("b2_bf16_bwd_gqa_n8192_d128_causal", 1, 32, 8, 8192, 128,
                                                   "bf16", True, seed=1302),
     "b3_bf16_bwd_n2048_d64": Workload("b3_bf16_bwd_n2048_d64", 4, 16, 16, 2048, 64, "bf16", False, seed=1303),
+    "b4_f16_bwd_n4096_d128_causal": Workload("b4_f16_bwd_n4096_d128_causal", 2, 32, 32, 4096, 128, "f16", True,
+                                             seed=1304),
 }
 
 
