@@ -465,8 +465,7 @@ def main(argv=None):
                          "kernel that reads and writes known byte counts, for scaling HBM counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the shard plan is in "
-              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU and has no multi-GPU path: run it with --gpus 1", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)

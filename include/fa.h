@@ -66,7 +66,7 @@ typedef enum fa_dtype {
 enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* bad pointer, size, flag, alignment or overlap */
-    FA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement   */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement  */
     FA_ERR_HIP = 3            /* the HIP runtime refused the launch            */
 };
 
@@ -96,7 +96,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_fwd_tiled: fa_fwd with an explicit tile shape (block_m query rows per
  * workgroup, block_n keys per K/V tile).  Used to show that the result does not
  * depend on the tiling (the pages' block-size invariance, kbwen.com feed "More
- * than two blocks").  Shapes this build does not hold return
+ * than two blocks").  Shapes the library does not hold return
  * FA_ERR_UNSUPPORTED; fa_tile_shapes lists the ones it does.
  */
 int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
