@@ -242,3 +242,12 @@ def test_measured_workloads_at_full_size(fa, oracle, name):
             what + " delta"
     for t in (dq, dk, dv, delta):
         assert torch.all(torch.isfinite(t.float())).item()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,splits", [(1, 8, 8, 1), (3, 8, 8, 2), (3, 24, 8, 3), (1, 16, 16, 1)])
+def test_every_gradient_under_each_block_order(fa, oracle, B, Hq, Hkv, splits):
+    """B*Hq and B*Hkv with one, an odd and an even number of heads per XCD, with and without
+    split dK/dV: every dq, dk and dv row is compared."""
+    q, k, v = fin.make_qkv(B, Hq, Hkv, 260, 64, "bf16", 500 + B + Hq)
+    do = fin.make_dout(B, Hq, 260, 64, "bf16", 501 + B + Hq)
+    compare(fa, oracle, q, k, v, do, True, 0.125, "bf16", "order B%d Hq%d Hkv%d" % (B, Hq, Hkv), splits)

@@ -326,3 +326,12 @@ def test_workload(fa, oracle, name):
         qf, kf = q.double()[0], k.double()[0]
         raw = (qf[:, :256] @ kf[:, :256].transpose(-1, -2)).abs().max()
         assert float(raw) > 89.0          # the unscaled q.k is beyond float32 exp's range
+
+
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 8, 8), (3, 8, 8), (1, 16, 4), (5, 8, 2), (2, 24, 8)])
+def test_every_row_under_each_block_order(fa, oracle, B, Hq, Hkv):
+    """Head counts that make the XCD block order walk one head per XCD, an odd number of
+    heads per XCD (one at a time) and even numbers (in pairs): every row of every head
+    must be written once, at every query tile, causal and not."""
+    for causal in (True, False):
+        parity(fa, oracle, B, Hq, Hkv, 384, 64, "bf16", causal, seed=B * 100 + Hq + Hkv)
