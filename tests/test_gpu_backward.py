@@ -142,15 +142,17 @@ def test_matches_the_oracle(fa, oracle, shape, d, causal, dtype):
     compare(fa, oracle, q, k, v, do, causal, 1.0 / np.sqrt(d), dtype, "%s d%d causal%d %s" % (shape, d, causal, dtype))
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("splits", [1, 2, 3, 8])
 @pytest.mark.parametrize("shape", [(1, 2, 1, 17), (1, 4, 2, 130), (2, 8, 2, 384), (1, 4, 1, 1000)])
-def test_split_dkdv_matches_the_oracle(fa, oracle, shape, splits):
+def test_split_dkdv_matches_the_oracle(fa, oracle, shape, splits, causal):
     """Each key tile's query tiles shared over 1-8 workgroups (some get none when a key
     tile has fewer tiles than splits) with fp32 partials summed in split order."""
     B, Hq, Hkv, N = shape
     q, k, v = fin.make_qkv(B, Hq, Hkv, N, 128, "bf16", 900 + N)
     do = fin.make_dout(B, Hq, N, 128, "bf16", 901 + N)
-    compare(fa, oracle, q, k, v, do, True, 1.0 / np.sqrt(128), "bf16", "%s split%d" % (shape, splits), splits)
+    compare(fa, oracle, q, k, v, do, causal, 1.0 / np.sqrt(128), "bf16",
+            "%s split%d causal%d" % (shape, splits, causal), splits)
 
 
 def test_split_dkdv_is_deterministic_and_matches_one_split(fa):
