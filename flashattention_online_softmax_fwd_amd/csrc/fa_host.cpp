@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "fa_kernels.h"
@@ -63,30 +64,43 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb)
     return x < y + nb && y < x + na;
 }
 
+// Checks shared by the attention entry points: head counts, head dimension, mask flag
+// and scale (which must stay finite once folded with log2(e)).  FA_OK or the error.
+int check_attention_args(int Hq, int Hkv, int d, int causal, float scale)
+{
+    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (!std::isfinite((float)((double)scale * 1.4426950408889634)))
+        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    return FA_OK;
+}
+
+// Every pointer non-null and 16-byte aligned.  FA_OK or the error.
+int check_pointers(std::initializer_list<const void*> ptrs)
+{
+    for (const void* ptr : ptrs)
+        if (!ptr) return fail(FA_ERR_INVALID_ARG, "null pointer");
+    for (const void* ptr : ptrs)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    return FA_OK;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
         int N, int d, int causal, float scale, int dtype, void* stream, int block_m, int block_n)
 {
     g_last_error.clear();
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
     if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
-    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
-    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
-    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
-    const double folded = (double)scale * 1.4426950408889634;   // scale * log2(e)
-    if (!std::isfinite((float)folded))
-        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    if (const int rc = check_attention_args(Hq, Hkv, d, causal, scale)) return rc;
     if ((block_m == 0) != (block_n == 0) || block_m < 0 || block_n < 0)
         return fail(FA_ERR_INVALID_ARG, "block_m and block_n must both be positive");
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (B == 0 || N == 0) return FA_OK;                         // empty output: nothing to do
-
-    if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null pointer");
-    const void* ptrs[5] = {q, k, v, o, lse};
-    for (const void* ptr : ptrs)
-        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (const int rc = check_pointers({q, k, v, o, lse})) return rc;
 
     const uint64_t esize = dtype == FA_DTYPE_F32 ? 4 : 2;
     const uint64_t qrows = (uint64_t)B * (uint64_t)Hq * (uint64_t)N;
@@ -130,7 +144,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.splits = 1;
     p.group = Hq / Hkv;
     p.n_qtiles = (int)ntiles;
-    p.scale_log2 = (float)folded;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
@@ -152,27 +166,16 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
     if (dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "split-KV is built for 16-bit inputs only");
     if (B < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARG, "B, Nq and Nk must be >= 0");
-    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
-    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
-    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (const int rc = check_attention_args(Hq, Hkv, d, causal, scale)) return rc;
     if (num_splits < 1 || num_splits > kMaxSplits)
         return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxSplits));
-    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
-    const double folded = (double)scale * 1.4426950408889634;   // scale * log2(e)
-    if (!std::isfinite((float)folded))
-        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (B == 0 || Nq == 0) return FA_OK;                        // no query row: nothing to do
     if (Nk == 0) return fail(FA_ERR_INVALID_ARG, "Nk must be >= 1 when there are query rows");
     if (causal && Nq > Nk)
         return fail(FA_ERR_INVALID_ARG, "causal needs Nq <= Nk (the queries are the last Nq positions)");
 
-    if (!q || !k || !v || !o_part || !lse_part) return fail(FA_ERR_INVALID_ARG, "null pointer");
-    const void* ptrs[5] = {q, k, v, o_part, lse_part};
-    for (const void* ptr : ptrs)
-        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (const int rc = check_pointers({q, k, v, o_part, lse_part})) return rc;
     const uint64_t qrows = (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq;
     const uint64_t qbytes = qrows * (uint64_t)d * 2;
     const uint64_t kvbytes = (uint64_t)B * (uint64_t)Hkv * (uint64_t)Nk * (uint64_t)d * 2;
@@ -214,7 +217,7 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     p.splits = num_splits;
     p.group = Hq / Hkv;
     p.n_qtiles = (int)ntiles;
-    p.scale_log2 = (float)folded;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
@@ -233,11 +236,7 @@ int run_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
         return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxSplits));
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (B == 0 || N == 0) return FA_OK;
-    if (!o_part || !lse_part || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null pointer");
-    const void* ptrs[4] = {o_part, lse_part, o, lse};
-    for (const void* ptr : ptrs)
-        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (const int rc = check_pointers({o_part, lse_part, o, lse})) return rc;
     const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
     const uint64_t pbytes = (uint64_t)num_splits * rows * (uint64_t)d * 4;
     const uint64_t plbytes = (uint64_t)num_splits * rows * 4;
@@ -303,13 +302,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
     if (dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "the backward is built for 16-bit inputs only");
     if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARG, "B and N must be >= 0");
-    if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1");
-    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-    if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1");
-    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
-    if (!std::isfinite((float)((double)scale * 1.4426950408889634)))
-        return fail(FA_ERR_INVALID_ARG, "scale * log2(e) overflows float32");
+    if (const int rc = check_attention_args(Hq, Hkv, d, causal, scale)) return rc;
     if (num_splits < 1 || num_splits > kMaxBwdSplits)
         return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxBwdSplits));
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
@@ -318,12 +311,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     if (num_splits > 1 && reinterpret_cast<uintptr_t>(dkv_part) % 16 != 0)
         return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
 
-    const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
-    for (const void* ptr : ptrs)
-        if (!ptr) return fail(FA_ERR_INVALID_ARG, "null pointer");
-    for (const void* ptr : ptrs)
-        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-            return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if (const int rc = check_pointers({q, k, v, o, lse, dout, dq, dk, dv, delta})) return rc;
     const uint64_t qrows = (uint64_t)B * (uint64_t)Hq * (uint64_t)N;
     const uint64_t qbytes = qrows * (uint64_t)d * 2;
     const uint64_t kvbytes = (uint64_t)B * (uint64_t)Hkv * (uint64_t)N * (uint64_t)d * 2;
