@@ -101,3 +101,56 @@ def test_single_key_closed_form():
     assert np.allclose(dv[0, 0], do[0].sum(0), atol=1e-15)
     assert np.all(np.abs(dq) < 1e-15) and np.all(np.abs(dk) < 1e-15)
     assert np.allclose(delta[0, :, 0], (do[0, :, 0] * v[0, 0, 0]).sum(-1), atol=1e-15)
+
+
+# Plausible mistakes planted in a copy of the backward oracle's source; each must fail a pin.
+MUTANTS = {
+    "no_delta": ("ds = p * (dp - dd[:, None])", "ds = p * dp"),
+    "delta_sign": ("ds = p * (dp - dd[:, None])", "ds = p * (dp + dd[:, None])"),
+    "ds_without_p": ("ds = p * (dp - dd[:, None])", "ds = (dp - dd[:, None])"),
+    "dq_unscaled": ("dq[b, h] = scale * (ds @ kh)", "dq[b, h] = ds @ kh"),
+    "dk_transposed_ds": ("dk[b, hk] += scale * (ds.T @ q[b, h])", "dk[b, hk] += scale * (ds @ q[b, h])"),
+    "dv_not_transposed": ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] += p @ do[b, h]"),
+    "gqa_overwrite": ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] = p.T @ do[b, h]"),
+    "dp_wrong_operand": ("dp = do[b, h] @ vh.T", "dp = do[b, h] @ kh.T"),
+    "mask_ignored": ("s[masked] = -np.inf", "pass"),
+    "delta_from_v": ("dd = (do[b, h] * o).sum(axis=1)", "dd = (do[b, h] * vh).sum(axis=1)"),
+}
+
+
+def _mutant(name):
+    import importlib.util
+    import inspect
+    src = inspect.getsource(backward_oracle)
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    spec = importlib.util.spec_from_loader("backward_oracle_" + name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new), "backward_oracle_" + name, "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_pass(mod):
+    """The pins above, as booleans: autograd on causal GQA and full shapes, and the identities."""
+    for case in [(1, 4, 2, 19, 8, True), (2, 2, 1, 13, 5, False)]:
+        B, Hq, Hkv, N, d, causal = case
+        q, k, v, do = _inputs(B, Hq, Hkv, N, d, 40 + N)
+        try:
+            dq, dk, dv, delta = mod.attention_backward(q, k, v, do, causal=causal, scale=0.4)
+        except Exception:
+            return False
+        gq, gk, gv, o = _autograd(q, k, v, do, causal, 0.4, Hq // Hkv)
+        if not (np.allclose(dq, gq, rtol=1e-9, atol=1e-10) and np.allclose(dk, gk, rtol=1e-9, atol=1e-10)
+                and np.allclose(dv, gv, rtol=1e-9, atol=1e-10)
+                and np.allclose(delta, (do * o).sum(-1), rtol=1e-10, atol=1e-10)):
+            return False
+    return True
+
+
+def test_the_pins_pass_the_oracle_itself():
+    assert _pins_pass(backward_oracle)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_every_planted_mistake_fails_a_pin(name):
+    assert not _pins_pass(_mutant(name)), name
