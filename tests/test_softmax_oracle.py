@@ -95,3 +95,45 @@ def test_bench_prices_each_algorithm_with_the_pages_access_counts():
     import bench
     g = _golden("p4_reading_once.json")
     assert {k: list(v) for k, v in bench.SOFTMAX_ACCESSES.items()} == g["reads_and_writes_per_element"]
+
+
+# Plausible mistakes planted in a copy of the oracle's source; each must fail one of the pins above.
+MUTANTS = {
+    "no_max_subtraction": ("e = np.exp(x - m)", "e = np.exp(x)"),
+    "min_instead_of_max": ("m = x.max(axis=1, keepdims=True)", "m = x.min(axis=1, keepdims=True)"),
+    "lse_without_m": ("lse = (m + np.log(l))[:, 0]", "lse = np.log(l)[:, 0]"),
+    "lse_log2": ("lse = (m + np.log(l))[:, 0]", "lse = (m + np.log2(l))[:, 0]"),
+    "not_normalised": ("y = e / l", "y = e"),
+    "sum_over_rows": ("l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
+    "empty_rows_zero": ("y[empty] = np.nan", "y[empty] = 0.0"),
+}
+
+
+def _mutant(name):
+    import importlib.util
+    import inspect
+    src = inspect.getsource(softmax_oracle)
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    spec = importlib.util.spec_from_loader("softmax_oracle_" + name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new), "softmax_oracle_" + name, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_every_planted_mistake_fails_a_pin(name, monkeypatch):
+    import warnings
+    monkeypatch.setattr(softmax_oracle, "softmax_rows", _mutant(name).softmax_rows)
+    pins = [test_five_scores_give_the_pages_probabilities, test_overflow_example_is_finite,
+            lambda: test_matches_library_softmax((5, 1000)), test_closed_forms,
+            test_masked_entries_and_empty_rows]
+    failed = 0
+    for pin in pins:
+        try:
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                pin()
+        except (AssertionError, FloatingPointError, ValueError):
+            failed += 1
+    assert failed >= 1, name
