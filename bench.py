@@ -48,8 +48,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def kernel_hash(source: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[source]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel's source file and the flags it is compiled with."""
+    from flashattention_online_softmax_fwd_amd import build
+
+    path = KERNEL_SOURCES[source]
+    with open(os.path.join(ROOT, path), "rb") as f:
+        data = f.read()
+    flags = " ".join(build.device_flags(os.path.basename(path))).encode()
+    return hashlib.sha256(data + b"\0" + flags).hexdigest()
 
 
 def traffic_for(workload: str, source: str):
@@ -57,7 +63,8 @@ def traffic_for(workload: str, source: str):
     workload, from committed rocprofv3 counters, or None.
 
     None when no counters were taken for this workload and kernel, or when the
-    kernel source changed since they were (its hash is stored next to them).
+    kernel's source or compile flags changed since they were (their hash is stored
+    next to them).
     """
     try:
         with open(TRAFFIC_FILE) as f:

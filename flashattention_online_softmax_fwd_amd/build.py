@@ -28,6 +28,17 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-Wall", "-Wno-unused-command-line-argument"]
 
 
+# Per-source additions.  The forward kernel's machine scheduler: the iterative ILP strategy
+# measured about 2% faster on the causal d = 128 forwards than the default (same code
+# otherwise, bitwise identical results).
+SOURCE_FLAGS = {"fa_fwd_mfma16.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-ilp"]}
+
+
+def device_flags(src: str) -> list:
+    """The hipcc flags a source is compiled with."""
+    return DEVICE_FLAGS + SOURCE_FLAGS.get(src, [])
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -37,7 +48,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + DEVICE_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + device_flags(src) + ["-I" + INCLUDE, "-I" + CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -21,9 +21,10 @@ HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shut
 def compile_asm(tmp_path_factory, source):
     if not HIPCC:
         pytest.skip("hipcc not available")
+    from flashattention_online_softmax_fwd_amd import build
     out = str(tmp_path_factory.mktemp("isa") / (source + ".s"))
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
-                    "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+    flags = [f for f in build.device_flags(source) if f != "-fPIC"]   # the library's own flags
+    subprocess.run([HIPCC] + flags + ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
                     "--offload-device-only", "-S", os.path.join(CSRC, source), "-o", out],
                    check=True, capture_output=True)
     return open(out).read()
