@@ -21,6 +21,7 @@ thread_local std::string g_last_error;
 
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxBwdSplits = 8;
+constexpr uint64_t kTileSlack = 128;   // rows a kernel may address past N in its last tile
 
 int fail(int code, const std::string& msg)
 {
@@ -109,8 +110,9 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const uint64_t kvbytes = kvrows * (uint64_t)d * esize;
     const uint64_t lbytes = qrows * 4;
     if (qbytes >> 62 || kvbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
-    // K/V tiles are read through buffer descriptors whose range is 32-bit
-    if ((uint64_t)N * (uint64_t)d * esize > 0x7fffffffULL)
+    // K/V tiles are read through buffer descriptors whose range and offsets are 32-bit;
+    // the offsets of the last tile's rows past N must stay below 2^31 as well
+    if (((uint64_t)N + kTileSlack) * (uint64_t)d * esize > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "one head of K or V exceeds 2 GiB");
     if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) ||
         overlaps(o, qbytes, v, kvbytes) || overlaps(lse, lbytes, q, qbytes) ||
@@ -182,7 +184,7 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     const uint64_t obytes = (uint64_t)num_splits * qrows * (uint64_t)d * 4;
     const uint64_t lbytes = (uint64_t)num_splits * qrows * 4;
     if (qbytes >> 62 || kvbytes >> 62 || obytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
-    if ((uint64_t)Nk * (uint64_t)d * 2 > 0x7fffffffULL)
+    if (((uint64_t)Nk + kTileSlack) * (uint64_t)d * 2 > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "one head of K or V exceeds 2 GiB");
     if (overlaps(o_part, obytes, q, qbytes) || overlaps(o_part, obytes, k, kvbytes) ||
         overlaps(o_part, obytes, v, kvbytes) || overlaps(lse_part, lbytes, q, qbytes) ||
@@ -317,7 +319,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     const uint64_t kvbytes = (uint64_t)B * (uint64_t)Hkv * (uint64_t)N * (uint64_t)d * 2;
     const uint64_t lbytes = qrows * 4;
     if (qbytes >> 62 || kvbytes >> 62) return fail(FA_ERR_INVALID_ARG, "problem too large");
-    if ((uint64_t)N * (uint64_t)d * 2 > 0x7fffffffULL)
+    if (((uint64_t)N + kTileSlack) * (uint64_t)d * 2 > 0x7fffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "one head of a tensor exceeds 2 GiB");
     const uint64_t kvelems = kvbytes / 2;
     const uint64_t pbytes = num_splits > 1 ? 2ULL * num_splits * kvelems * 4 : 0;   // fp32 partials

@@ -263,3 +263,14 @@ def test_bwd_split_needs_no_workspace_for_one_split_and_sizes(lib):
     assert lib.fa_bwd_num_splits(2, 32, 32, 4096) == 1
     assert lib.fa_bwd_num_splits(1, 1, 1, 128) == 8
     assert lib.fa_bwd_num_splits(0, 1, 1, 1) == -1 and lib.fa_bwd_num_splits(1, 3, 2, 8) == -1
+
+
+def test_head_size_limit_leaves_room_for_the_last_tile(lib):
+    """Tiles address up to 128 rows past N through 32-bit buffer offsets: a head whose K/V
+    with that slack would pass 2^31 - 1 bytes is refused before any HIP call (only the
+    refused side is called here: the accepted side would launch)."""
+    n_over = (0x7FFFFFFF // 256) - 128 + 1          # d = 128, 2-byte elements: 256 B rows
+    assert call(lib, N=n_over, d=128, B=1, Hq=1, Hkv=1) == 2
+    assert b"2 GiB" in lib.fa_last_error()
+    assert call_split(lib, Nq=1, Nk=n_over, d=128, Hq=1, Hkv=1, causal=0) == 2
+    assert call_bwd(lib, N=n_over, d=128, Hq=1, Hkv=1) == 2
