@@ -253,3 +253,29 @@ def test_every_gradient_under_each_block_order(fa, oracle, B, Hq, Hkv, splits):
     q, k, v = fin.make_qkv(B, Hq, Hkv, 260, 64, "bf16", 500 + B + Hq)
     do = fin.make_dout(B, Hq, 260, 64, "bf16", 501 + B + Hq)
     compare(fa, oracle, q, k, v, do, True, 0.125, "bf16", "order B%d Hq%d Hkv%d" % (B, Hq, Hkv), splits)
+
+
+def _random_cases(count, seed):
+    """Seeded random shapes within a size budget (B*Hq*N^2 <= 6e6), both dtypes and masks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        N = int(rng.integers(1, 1200))
+        if B * Hkv * G * N * N > 6e6:
+            continue
+        out.append((B, G * Hkv, Hkv, N, int(rng.choice([64, 128])), str(rng.choice(["bf16", "f16"])),
+                    bool(rng.integers(0, 2)), int(rng.integers(1, 9))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 2024))
+def test_random_shapes(fa, oracle, case):
+    """Forward output, LSE and all three gradients on seeded random shapes, split counts and masks."""
+    B, Hq, Hkv, N, d, dtype, causal, splits = case
+    seed = (B * 131 + Hq * 17 + N * 7 + d) % 100000
+    q, k, v = fin.make_qkv(B, Hq, Hkv, N, d, dtype, seed)
+    do = fin.make_dout(B, Hq, N, d, dtype, seed + 1)
+    compare(fa, oracle, q, k, v, do, causal, 1.0 / np.sqrt(d), dtype, "random %s" % (case,), splits)
