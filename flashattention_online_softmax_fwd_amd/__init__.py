@@ -61,24 +61,10 @@ def forward(q, k, v, causal=False, scale=None, block_m=None, block_n=None, out=N
     given to write into existing tensors.  Runs on torch's current stream.
     """
     lib = _lib.load()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("%s must be a torch.Tensor" % name)
-        if t.dim() != 4:
-            raise ValueError("%s must be 4-D [B, H, N, d], got %s" % (name, tuple(t.shape)))
-        if not t.is_cuda:
-            raise ValueError("%s must be a CUDA (HIP) tensor" % name)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k and v must share one dtype")
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k and v must be on one device")
-    if q.dtype not in _DTYPES:
-        raise ValueError("dtype %s is not supported" % q.dtype)
+    _check_inputs(q, k, v)
     B, Hq, N, d = q.shape
-    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or v.shape != k.shape:
-        raise ValueError("k and v must be [B, Hkv, N, d] matching q; got %s, %s, %s"
+    if k.shape[2] != N:
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's N; got %s, %s, %s"
                          % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     Hkv = k.shape[1]
     if scale is None:

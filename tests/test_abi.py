@@ -127,6 +127,10 @@ def test_python_wrapper_checks_before_the_library():
         fa.forward(x, x, x)                     # CPU tensors are refused
     with pytest.raises(ValueError):
         fa.forward(torch.zeros(4, 64), x, x)    # wrong rank
+    with pytest.raises(TypeError):
+        fa.forward([0.0], x, x)                 # not a tensor
+    with pytest.raises(ValueError):
+        fa.backward(x, x, x, x, torch.zeros(1, 1, 4), x)   # CPU tensors are refused here too
 
 
 def call_split(lib, q=P, k=P + 0x100000, v=P + 0x200000, op=P + 0x300000, lp=P + 0x500000, B=1, Hq=2,
