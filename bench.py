@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "bwd": "flashattention_online_softmax_fwd_amd/csrc/fa_bwd_mfma16.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
 
 
 def kernel_hash(source: str) -> str:
@@ -75,6 +76,25 @@ def traffic_for(workload: str, source: str):
     if not entry or entry.get("kernel_source_sha256") != kernel_hash(source):
         return None
     return entry.get("traffic_bytes_per_launch")
+
+
+def counters_for(workload: str, source: str):
+    """Shader counters of the kernel built from KERNEL_SOURCES[source] on this workload, from
+    a committed rocprofv3 pass: the kernel's own shader clock, MFMA busy share at that clock,
+    LDS activity and bank conflicts.  None when absent or when the kernel changed since."""
+    try:
+        with open(SQ_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = table.get(workload, {}).get(source)
+    if not entry or entry.get("kernel_source_sha256") != kernel_hash(source):
+        return None
+    keys = ("sclk_ghz", "mfma_busy", "mfma_insts_over_algorithmic", "valu_insts_per_mfma",
+            "lds_insts_per_mfma", "lds_idx_active", "lds_bank_conflict_rate", "kernel_us_under_counters")
+    out = {k: entry[k] for k in keys if k in entry}
+    out["source"] = "rocprofv3 --pmc (profiles/sq_counters.json)"
+    return out
 
 
 def time_gpu(fa, q, k, v, w, steps, warmup):
@@ -206,6 +226,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget):
             "algorithmic_flops_per_launch": w.flops,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
         },
+        "counters": counters_for(w.name, w.dtype),
     }
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, o, lse, cpu_budget)

@@ -28,3 +28,15 @@ def test_kernel_hash_covers_sources_and_flags():
     assert h == bench.kernel_hash("f16")        # one source, one set of flags
     assert h != bench.kernel_hash("bwd")
     assert h != bench.kernel_hash("f32")
+
+
+def test_committed_shader_counters_are_read_and_go_stale_with_the_kernel(monkeypatch):
+    c = bench.counters_for("c3_bf16_n4096_d128_causal", "bf16")
+    assert c is not None
+    assert 0.0 < c["mfma_busy"] <= 1.0
+    assert 0.5 < c["sclk_ghz"] < 2.6
+    assert c["lds_bank_conflict_rate"] >= 0.0
+    assert bench.counters_for("no_such_workload", "bf16") is None
+    monkeypatch.setattr(bench, "kernel_hash", lambda source: "0" * 64)
+    assert bench.counters_for("c3_bf16_n4096_d128_causal", "bf16") is None
+    assert bench.traffic_for("c3_bf16_n4096_d128_causal", "bf16") is None
