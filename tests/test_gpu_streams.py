@@ -110,3 +110,19 @@ def test_error_messages_are_per_thread(fa):
         t.join(timeout=60)
     assert seen["bad"][0] == fa.FA_ERR_INVALID_ARG and "causal" in seen["bad"][1]
     assert seen["good"] == (fa.FA_OK, "")
+
+
+@pytest.mark.parametrize("bad", [dict(causal=2), dict(Hkv=3), dict(d=96), dict(scale=float("inf")), dict(dtype=7)])
+def test_refused_calls_leave_the_outputs_untouched(fa, bad):
+    (q, k, v), _ = problems()[0]
+    o = torch.full_like(q, 7.0)
+    lse = torch.full(q.shape[:3], -3.0, dtype=torch.float32, device=q.device)
+    B, Hq, N, d = q.shape
+    args = dict(B=B, Hq=Hq, Hkv=k.shape[1], N=N, d=d, causal=1, scale=0.125, dtype=fa.FA_DTYPE_BF16)
+    args.update(bad)
+    rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), args["B"], args["Hq"],
+                   args["Hkv"], args["N"], args["d"], args["causal"], args["scale"], args["dtype"], None)
+    torch.cuda.synchronize()
+    assert rc in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED)
+    assert fa.fa_last_error() != ""
+    assert bool((o == 7.0).all()) and bool((lse == -3.0).all())
