@@ -214,6 +214,21 @@ def make_qkv(B, Hq, Hkv, N, d, dtype="bf16", seed=0, q_mult=1.0, Nk=None):
     return (torch.from_numpy(q).to(td), torch.from_numpy(k).to(td), torch.from_numpy(v).to(td))
 
 
+def make_qkv_device(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=0, device="cuda"):
+    """Seeded Q, K, V drawn on a device (torch's Philox generator there), for problems whose
+    K/V are too large to draw on the host in reasonable time.  Standard normals rounded to the
+    input dtype; deterministic for a given seed and device type."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch_dtype(dtype)
+    q = torch.randn((B, Hq, Nq, d), generator=g, device=device, dtype=torch.float32).to(td)
+    k = torch.randn((B, Hkv, Nk, d), generator=g, device=device, dtype=torch.float32).to(td)
+    v = torch.randn((B, Hkv, Nk, d), generator=g, device=device, dtype=torch.float32).to(td)
+    return q, k, v
+
+
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.q_mult)
 

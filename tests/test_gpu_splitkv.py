@@ -175,3 +175,40 @@ def test_measured_workloads_at_full_size(fa, oracle, name):
     ro, rl = oracle.attention_kv(q, k, v, causal=w.causal, scale=w.softmax_scale, rows=rows)
     check(o.reshape(-1, w.d).numpy()[rows], ro, *BF16, "O " + name)
     check(lse.reshape(-1).numpy()[rows], rl, *BF16, "LSE " + name)
+
+
+def test_longest_key_head_the_abi_accepts(fa, oracle):
+    """One decode row against the longest K/V head the ABI takes at d = 128: (Nk + 128) d 2 bytes
+    just below 2^31.  With one key range a single workgroup walks the whole head, so its buffer
+    range and the last tile's offsets are the largest any launch can use; the default split count
+    is checked too.  Four keys score far above the 8.4M others (16 to 17.5 against about N(0, 1))
+    and carry distinct value rows: the first key, the middle one, one in the last tile and the very
+    last, so a range cut short or mis-addressed near its end moves O far past the bar.  One key
+    more is refused before anything is launched."""
+    d = 128
+    nk = 0x7FFFFFFF // (2 * d) - 128
+    print("longest accepted head: Nk", nk, flush=True)
+    q, k, v = fin.make_qkv_device(1, 1, 1, 1, nk, d, "bf16", seed=1201)
+    scale = 1.0 / math.sqrt(d)
+    qf = q.float().reshape(d)
+    spikes = [(0, 16.0), (nk // 2, 16.5), (nk - 65, 17.0), (nk - 1, 17.5)]
+    for n, (pos, target) in enumerate(spikes):
+        k[0, 0, pos] = (qf * (target / (scale * float(qf @ qf)))).to(torch.bfloat16)
+        row = torch.zeros(d, device=v.device)
+        row[8 * n + 3] = 8.0
+        v[0, 0, pos] = row.to(torch.bfloat16)
+    results = {}
+    for S in (1, fa.fa_splitkv_num_splits(1, 1, 1, 1, nk)):
+        results[S] = fa.attention_kv(q, k, v, causal=True, num_splits=S)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kv(q.cpu(), k.cpu(), v.cpu(), causal=True, scale=scale)
+    for n in range(len(spikes)):   # every planted key carries a visible share of O
+        assert ro[0, 0, 0, 8 * n + 3] > 0.4, (n, ro[0, 0, 0, 8 * n + 3])
+    for S, (o, lse) in results.items():
+        check(o.float().cpu().numpy(), ro, *BF16, "O at the longest head, %d ranges" % S)
+        check(lse.cpu().numpy(), rl, *BF16, "LSE at the longest head, %d ranges" % S)
+    op = torch.empty((1, 1, 1, 1, d), dtype=torch.float32, device=q.device)
+    lp = torch.empty((1, 1, 1, 1), dtype=torch.float32, device=q.device)
+    rc = fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), op.data_ptr(), lp.data_ptr(),
+                           1, 1, 1, 1, nk + 1, d, 1, scale, fa.FA_DTYPE_BF16, 1, None)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "2 GiB" in fa.fa_last_error()
