@@ -22,6 +22,7 @@ thread_local std::string g_last_error;
 constexpr int kMaxSplits = 1024;
 constexpr int kMaxBwdSplits = 8;
 constexpr uint64_t kTileSlack = 128;   // rows a kernel may address past N in its last tile
+constexpr int kMaxSoftmaxCols = 0x7fffffff - 4095;   // 2^31 - 4096
 
 int fail(int code, const std::string& msg)
 {
@@ -273,6 +274,8 @@ int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, in
     if (rows == 0) return FA_OK;
     if (cols == 0) return fail(FA_ERR_INVALID_ARG, "a row needs at least one entry (cols >= 1)");
     if (rows > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "more than 2^31 - 1 rows");
+    // the kernels step 32-bit column indices 1024 vectors at a time; this keeps every step below 2^31
+    if (cols > kMaxSoftmaxCols) return fail(FA_ERR_UNSUPPORTED, "more than 2^31 - 4096 columns");
     if (!x || !y) return fail(FA_ERR_INVALID_ARG, "null pointer");
     if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(y) % 16 != 0 ||
         (lse && reinterpret_cast<uintptr_t>(lse) % 16 != 0))

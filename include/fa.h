@@ -188,7 +188,8 @@ enum {
  *             FA_DTYPE_BF16 or FA_DTYPE_F16 (both the same dtype; the arithmetic is
  *             fp32); y may be x itself (in place) but must not otherwise overlap it
  *   lse       device pointer, [rows] float32, written; may be NULL
- *   rows      0 .. 2^31 - 1 (0: FA_OK, nothing touched); cols >= 1
+ *   rows      0 .. 2^31 - 1 (0: FA_OK, nothing touched)
+ *   cols      1 .. 2^31 - 4096 (longer rows: FA_ERR_UNSUPPORTED)
  *   algo      FA_SOFTMAX_ONLINE or FA_SOFTMAX_SAFE (same result up to rounding)
  * A row whose entries are all -inf has no softmax: its y is nan and its lse -inf.
  * Ownership, alignment (16 bytes for x, y and lse) and error rules as for fa_fwd.

@@ -198,6 +198,8 @@ def test_split_chunk_and_default_splits(lib):
     ((P, P + 0x40, 0, 4, 64, 0, 0), 1),                       # y overlaps x without being x
     ((P, P + 0x100000, P + 0x20, 4, 64, 0, 0), 1),            # lse overlaps x
     ((P, P + 0x100000, 0, 1 << 31, 64, 0, 0), 2),             # too many rows for the grid
+    ((P, P, 0, 1, (1 << 31) - 4095, 0, 0), 2),                # one column past the 32-bit index limit
+    ((P, P, 0, 1, (1 << 31) - 1, 0, 0), 2),
 ])
 def test_softmax_rejects_bad_arguments(lib, args, code):
     assert lib.fa_softmax(*args, None) == code
