@@ -199,8 +199,12 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     for (int i = 0; i < split_n && !e; ++i)
         if (split_table[i].d == d && split_table[i].causal == causal) e = &split_table[i];
     if (!e) return fail(FA_ERR_UNSUPPORTED, "no split-KV kernel for this d");
-    // the G query heads of a K/V head share its workgroups: G*Nq packed rows per K/V head
-    const uint64_t ntiles = ((uint64_t)(Hq / Hkv) * (uint64_t)Nq + e->block_m - 1) / e->block_m;
+    // the G query heads of a K/V head share its workgroups: G*Nq packed rows per K/V head,
+    // indexed in 32 bits by the kernel (its last tile may reach block_m rows past them)
+    const uint64_t packed = (uint64_t)(Hq / Hkv) * (uint64_t)Nq;
+    if (packed + (uint64_t)e->block_m > 0x7fffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "more than 2^31 - 129 query rows per K/V head (G * Nq)");
+    const uint64_t ntiles = (packed + e->block_m - 1) / e->block_m;
     const uint64_t grid = (uint64_t)num_splits * (uint64_t)B * (uint64_t)Hkv * ntiles;
     if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
 

@@ -132,7 +132,9 @@ int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap);
  *   lse_part  [num_splits][B][Hq][Nq] float32 (written): m + ln l of that state;
  *             a row with no visible key in the range gets lse = -inf and o = 0
  *             (the empty state, which carries no weight in the merge)
- *   B, Nq     >= 0 (0: FA_OK, nothing touched); Nk >= 1 when Nq >= 1
+ *   B, Nq     >= 0 (0: FA_OK, nothing touched); Nk >= 1 when Nq >= 1;
+ *             (Hq / Hkv) * Nq <= 2^31 - 129 and (Nk + 128) * d * 2 < 2^31
+ *             (else FA_ERR_UNSUPPORTED)
  *   Hq, Hkv, d, scale, stream: as for fa_fwd; dtype FA_DTYPE_BF16 or
  *             FA_DTYPE_F16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED)
  * Ownership, alignment, overlap and error rules as for fa_fwd (o_part and lse_part

@@ -147,6 +147,8 @@ def call_split(lib, q=P, k=P + 0x100000, v=P + 0x200000, op=P + 0x300000, lp=P +
     (dict(dtype=0), 2), (dict(dtype=9), 1), (dict(d=96), 2),
     (dict(op=P + 0x100000), 1),                           # o_part overlaps k
     (dict(lp=P + 0x300010), 1),                           # lse_part overlaps o_part
+    (dict(Hq=64, Hkv=1, Nq=1 << 25, causal=0, k=P + (1 << 40), v=P + (2 << 40),
+          op=P + (4 << 40), lp=P + (8 << 40)), 2),        # G * Nq = 2^31 packed rows per K/V head
 ])
 def test_splitkv_rejects_bad_arguments_before_any_hip_call(lib, kw, code):
     assert call_split(lib, **kw) == code
