@@ -335,3 +335,18 @@ def test_every_row_under_each_block_order(fa, oracle, B, Hq, Hkv):
     must be written once, at every query tile, causal and not."""
     for causal in (True, False):
         parity(fa, oracle, B, Hq, Hkv, 384, 64, "bf16", causal, seed=B * 100 + Hq + Hkv)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(256, 64, 8, 1), (128, 64, 64, 3), (97, 8, 8, 1)])
+def test_many_heads_of_few_keys(fa, oracle, B, Hq, Hkv, N):
+    """Thousands of (batch, head) units of one to three keys: the block order must reach every
+    unit exactly once (16384, 8192 and 776 units: paired, paired and one-at-a-time XCD walks).
+    With one key, O is that key's value exactly."""
+    q, k, v = fin.make_qkv(B, Hq, Hkv, N, 128, "bf16", seed=B + Hq + N)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_gpu(fa, q, k, v, True, scale)
+    if N == 1:
+        assert torch.equal(o, v.float().repeat_interleave(Hq // Hkv, dim=1))
+    ro, rl = oracle.attention(q, k, v, causal=True, scale=scale)
+    check(o.numpy(), ro, "bf16", "O many heads")
+    check(lse.numpy(), rl, "bf16", "LSE many heads")
