@@ -79,7 +79,8 @@ def traffic_for(workload: str, source: str):
 
 
 def counters_for(workload: str, source: str):
-    """Shader counters of the kernel built from KERNEL_SOURCES[source] on this workload, from
+    """Shader counters of the kernel built from KERNEL_SOURCES[source] (or of one kernel of it,
+    "source/part") on this workload, from
     a committed rocprofv3 pass: the kernel's own shader clock, MFMA busy share at that clock,
     LDS activity and bank conflicts.  None when absent or when the kernel changed since."""
     try:
@@ -87,8 +88,8 @@ def counters_for(workload: str, source: str):
             table = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = table.get(workload, {}).get(source)
-    if not entry or entry.get("kernel_source_sha256") != kernel_hash(source):
+    entry = table.get(workload, {}).get(source)   # "bwd/dq": one kernel of a multi-kernel source
+    if not entry or entry.get("kernel_source_sha256") != kernel_hash(source.split("/")[0]):
         return None
     keys = ("sclk_ghz", "mfma_busy", "mfma_insts_over_algorithmic", "valu_insts_per_mfma",
             "lds_insts_per_mfma", "lds_idx_active", "lds_bank_conflict_rate", "kernel_us_under_counters")
@@ -472,6 +473,7 @@ def run_bwd_workload(name, steps, warmup):
                      "frac": achieved / peak, "traffic": traffic_for(w.name, "bwd"),
                      "kernel": "fa_bwd_split (fa::bwd_dq_kernel + fa::bwd_dkdv_kernel [+ fa::bwd_reduce_kernel])",
                      "avg_launch_ms": ms, "algorithmic_flops_per_launch": flops},
+        "counters": {part: counters_for(w.name, "bwd/" + part) for part in ("dq", "dkdv")},
     }
 
 

@@ -40,3 +40,9 @@ def test_committed_shader_counters_are_read_and_go_stale_with_the_kernel(monkeyp
     monkeypatch.setattr(bench, "kernel_hash", lambda source: "0" * 64)
     assert bench.counters_for("c3_bf16_n4096_d128_causal", "bf16") is None
     assert bench.traffic_for("c3_bf16_n4096_d128_causal", "bf16") is None
+
+
+def test_backward_counters_are_keyed_per_kernel():
+    for part in ("dq", "dkdv"):
+        c = bench.counters_for("b1_bf16_bwd_n4096_d128_causal", "bwd/" + part)
+        assert c is not None and 0.0 < c["mfma_busy"] <= 1.0
