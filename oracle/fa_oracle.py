@@ -163,8 +163,8 @@ def merge_partials(o_parts, lse_parts):
     o_parts [S, ..., d] and lse_parts [S, ...]: state s in normalised form
     (o = acc / l, lse = m + ln l; lse = -inf for an empty state).  Each state is
     read as (m, l, acc) = (lse, 1, o), the same state measured against m + ln l,
-    and the S states are folded with the pages' merge (``online_model.merge``:
-    take the larger max, rescale each side by exp(its max - that max), add;
+    and the S states are pooled with the pages' merge (``online_model.merge``:
+    take the largest max, rescale each state by exp(its max - that max), add;
     spicyshark.co lesson, "From softmax to attention" and "Check yourself").
     Returns (o, lse) of the union; a row whose states are all empty gives o = 0,
     lse = -inf.
@@ -183,11 +183,8 @@ def merge_partials(o_parts, lse_parts):
     out_o = np.zeros((R, d), dtype=np.float64)
     out_l = np.full((R,), -np.inf, dtype=np.float64)
     for r in range(R):
-        state = (-np.inf, 0.0, np.zeros(d))
-        for s in range(S):
-            m_s = flat_l[s, r]
-            part = (m_s, 1.0, flat_o[s, r]) if m_s > -np.inf else (-np.inf, 0.0, np.zeros(d))
-            state = online_model.merge(state, part)
+        parts = [(flat_l[s, r], 1.0, flat_o[s, r]) for s in range(S)]
+        state = online_model.merge(*parts)
         m, l, acc = state
         if l > 0.0:
             out_o[r] = np.asarray(acc) / l
