@@ -34,6 +34,9 @@ _FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]
 SIGNATURES = {
     "fa_fwd": (_I, _FWD_ARGS),
     "fa_fwd_tiled": (_I, _FWD_ARGS + [_I, _I]),
+    "fa_fwd_stamped": (_I, _FWD_ARGS + [_P, ctypes.c_longlong]),
+    "fa_fwd_stamp_slots": (ctypes.c_longlong, [_I, _I, _I, _I, _I]),
+    "fa_wall_clock_khz": (_I, [_I]),
     "fa_tile_shapes": (_I, [_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P]),
     "fa_merge": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -79,6 +82,19 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream):
 def fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, block_m, block_n):
     return load().fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream,
                                block_m, block_n)
+
+
+def fa_fwd_stamped(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, stamps, stamp_slots):
+    return load().fa_fwd_stamped(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, stamps,
+                                 stamp_slots)
+
+
+def fa_fwd_stamp_slots(B, Hq, N, d, dtype):
+    return load().fa_fwd_stamp_slots(B, Hq, N, d, dtype)
+
+
+def fa_wall_clock_khz(device):
+    return load().fa_wall_clock_khz(device)
 
 
 def fa_fwd_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,

@@ -126,6 +126,13 @@ fwd16_kernel(const FwdParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    // Optional clock stamps of this wave: the constant-rate real-time counter and the
+    // shader-cycle counter, read at the start and at the end of the wave's work.
+    unsigned long long real0 = 0, cyc0 = 0;
+    if (!SPLIT && p.stamps) {
+        real0 = __builtin_amdgcn_s_memrealtime();
+        cyc0 = __builtin_amdgcn_s_memtime();
+    }
     const int l32 = lane & 31;
     const int hi = lane >> 5;
     const int q0 = qt * BM;
@@ -416,6 +423,12 @@ fwd16_kernel(const FwdParams p)
                 *(ex4*)(Orow + 32 * dt + 8 * g + 4 * hi) = w;
             }
         if (hi == 0) p.lse[(size_t)bh * N + my_q] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    if (p.stamps && lane == 0) {
+        const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
+        const unsigned long long real1 = __builtin_amdgcn_s_memrealtime();
+        typedef __attribute__((ext_vector_type(4))) unsigned long long u64x4;
+        *(u64x4*)(p.stamps + ((size_t)bid * NW + wave) * 4) = u64x4{real0, real1, cyc0, cyc1};
     }
 }
 

@@ -92,7 +92,8 @@ int check_pointers(std::initializer_list<const void*> ptrs)
 }
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-        int N, int d, int causal, float scale, int dtype, void* stream, int block_m, int block_n)
+        int N, int d, int causal, float scale, int dtype, void* stream, int block_m, int block_n,
+        unsigned long long* stamps = nullptr, long long stamp_slots = 0)
 {
     g_last_error.clear();
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
@@ -130,6 +131,15 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const uint64_t ntiles = ((uint64_t)N + e->block_m - 1) / e->block_m;
     const uint64_t grid = (uint64_t)B * (uint64_t)Hq * ntiles;
     if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if (stamps) {
+        const uint64_t slots = grid * (uint64_t)(e->block_m / 32);   // one per wave of 32 rows
+        if (stamp_slots < 0 || (uint64_t)stamp_slots < slots)
+            return fail(FA_ERR_INVALID_ARG, "stamps holds fewer slots than the launch has waves");
+        if (overlaps(stamps, slots * 32, q, qbytes) || overlaps(stamps, slots * 32, k, kvbytes) ||
+            overlaps(stamps, slots * 32, v, kvbytes) || overlaps(stamps, slots * 32, o, qbytes) ||
+            overlaps(stamps, slots * 32, lse, lbytes))
+            return fail(FA_ERR_INVALID_ARG, "stamps must not overlap the inputs or outputs");
+    }
 
     fa::FwdParams p;
     p.q = q;
@@ -149,6 +159,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
+    p.stamps = stamps;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;
@@ -226,6 +237,7 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
+    p.stamps = nullptr;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;
@@ -418,6 +430,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, 0, 0);
 }
 
+int fa_fwd_stamped(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                   int N, int d, int causal, float scale, int dtype, void* stream, unsigned long long* stamps,
+                   long long stamp_slots)
+{
+    g_last_error.clear();
+    if (dtype == FA_DTYPE_F32) {
+        g_last_error = "clock stamps are built into the 16-bit kernels only";
+        return FA_ERR_UNSUPPORTED;
+    }
+    if (!stamps || reinterpret_cast<uintptr_t>(stamps) % 32 != 0) {
+        g_last_error = "stamps must be a non-null, 32-byte aligned device pointer";
+        return FA_ERR_INVALID_ARG;
+    }
+    return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream, 0, 0, stamps, stamp_slots);
+}
+
+long long fa_fwd_stamp_slots(int B, int Hq, int N, int d, int dtype)
+{
+    if (B < 0 || Hq < 1 || N < 0 || (d != 64 && d != 128)) return -1;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return -1;
+    const fa::KernelEntry* e = find_kernel(dtype, d, 0, 0, 0);
+    if (!e) return -1;
+    return (long long)B * Hq * (((long long)N + e->block_m - 1) / e->block_m) * (e->block_m / 32);
+}
+
+int fa_wall_clock_khz(int device)
+{
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
+    return khz;
+}
+
 int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                  int Hkv, int N, int d, int causal, float scale, int dtype, void* stream, int block_m,
                  int block_n)
@@ -499,7 +543,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 5;
+    return 6;
 }
 
 }  // extern "C"

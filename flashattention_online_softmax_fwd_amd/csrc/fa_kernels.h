@@ -22,6 +22,9 @@ struct FwdParams {
     int n_qtiles;    // ceil(N / block_m)
     float scale_log2;  // scale * log2(e): scores go straight to the exp2 domain
     int xcd_map;       // 1: block order spreads whole heads over the 8 XCDs (set by the launcher)
+    // Square 16-bit forward only, else null: per wave {real-time start, real-time end,
+    // shader-cycle start, shader-cycle end}, at [(block * waves + wave) * 4].
+    unsigned long long* stamps;
 };
 
 using Launcher = hipError_t (*)(const FwdParams&, hipStream_t);

@@ -34,7 +34,7 @@ class Workload:
     q_mult: float = 1.0
     scale: float | None = None   # None: 1/sqrt(d)
     seed: int = 0
-    oracle_rows: int | None = None   # sampled rows for the oracle (None: all)
+    oracle_rows: int | None = None   # rows the parity test samples for the oracle (None: every row)
 
     @property
     def softmax_scale(self) -> float:
@@ -66,7 +66,7 @@ WORKLOADS = {
     "c4_bf16_gqa_n8192_d128_causal": Workload("c4_bf16_gqa_n8192_d128_causal", 1, 32, 8, 8192, 128,
                                               "bf16", True, seed=1004),
     "c5_bf16_n32768_d128_causal_q12": Workload("c5_bf16_n32768_d128_causal_q12", 1, 8, 8, 32768, 128,
-                                               "bf16", True, q_mult=12.0, seed=1005, oracle_rows=512),
+                                               "bf16", True, q_mult=12.0, seed=1005, oracle_rows=32768),
     "c5s_bf16_n4096_d128_causal_q12_scale1": Workload("c5s_bf16_n4096_d128_causal_q12_scale1", 1, 8, 8,
                                                       4096, 128, "bf16", True, q_mult=12.0, scale=1.0,
                                                       seed=1006),

@@ -81,8 +81,13 @@ enum {
  *   Hq, Hkv   >= 1 with Hq % Hkv == 0
  *   d         64 or 128 (other positive values: FA_ERR_UNSUPPORTED)
  *   causal    0 or 1
- *   scale     any finite float; multiplies q.k before the softmax
- *             (1/sqrt(d) gives the usual attention)
+ *   scale     any finite float whose product with log2(e) is finite in float32;
+ *             multiplies q.k before the softmax (1/sqrt(d) gives the usual
+ *             attention).  The scaled scores scale * q.k of visible pairs must
+ *             stay below 2^29 in magnitude: the kernels subtract the row maximum
+ *             after scaling, in float32, and beyond that the maximum's own
+ *             rounding can overflow the exponentials (a 0 scale gives uniform
+ *             weights; a negative one reverses the order of the scores)
  *   dtype     FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16
  *   stream    hipStream_t to enqueue on; NULL means the default stream
  *
@@ -102,6 +107,36 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                  int dtype, void* stream, int block_m, int block_n);
+
+/*
+ * fa_fwd_stamped: fa_fwd (bf16 or fp16, default tile) that also records when each
+ * wave of the launch ran, for measuring the shader clock the kernel actually ran
+ * at and the spread of work over the grid.  Not part of the method: the pages
+ * give no hardware figures; this is the measurement side of the forward.
+ *
+ *   stamps       device pointer, 32-byte aligned, at least stamp_slots * 4
+ *                unsigned 64-bit words, written: for wave w of the launch,
+ *                stamps[4w + 0], [4w + 1] = the constant-rate real-time counter
+ *                (fa_wall_clock_khz kHz) when the wave started and ended;
+ *                stamps[4w + 2], [4w + 3] = the shader-cycle counter at the same
+ *                two points, so (cycles / real-time ticks) * wall clock rate is the
+ *                wave's average shader clock.  Must not overlap any other argument.
+ *   stamp_slots  the buffer's capacity in waves; fa_fwd_stamp_slots gives the
+ *                number the launch has (fewer: FA_ERR_INVALID_ARG)
+ *   other arguments, ownership and errors: as for fa_fwd; FA_DTYPE_F32 returns
+ *   FA_ERR_UNSUPPORTED.  o and lse are bitwise the same as fa_fwd's.
+ */
+int fa_fwd_stamped(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   int dtype, void* stream, unsigned long long* stamps, long long stamp_slots);
+
+/* Waves of an fa_fwd launch of this shape (16-bit dtypes), i.e. the slots
+ * fa_fwd_stamped writes; -1 for a bad size or dtype. */
+long long fa_fwd_stamp_slots(int B, int Hq, int N, int d, int dtype);
+
+/* Rate of the real-time counter of device `device` in kHz (hipDeviceAttributeWallClockRate),
+ * or -1 if the runtime does not report it. */
+int fa_wall_clock_khz(int device);
 
 /*
  * fa_tile_shapes: the (block_m, block_n) pairs compiled for (dtype, d).
@@ -260,7 +295,7 @@ const char* fa_error_string(int code);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

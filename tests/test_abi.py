@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
                           "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
                           "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax", "fa_bwd", "fa_bwd_split",
-                          "fa_bwd_num_splits"}
+                          "fa_bwd_num_splits", "fa_fwd_stamped", "fa_fwd_stamp_slots", "fa_wall_clock_khz"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -65,7 +65,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -103,6 +103,32 @@ def call(lib, q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400
 ])
 def test_invalid_arguments_are_rejected_before_any_hip_call(lib, kw, code):
     assert call(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_stamp_slots_count_the_waves_of_the_default_tile(lib):
+    from flashattention_online_softmax_fwd_amd import _lib
+    for dtype in (1, 2):
+        bm = _lib.fa_tile_shapes(dtype, 128)[0][0]
+        assert lib.fa_fwd_stamp_slots(2, 32, 4096, 128, dtype) == 2 * 32 * (4096 // bm) * (bm // 32)
+        assert lib.fa_fwd_stamp_slots(1, 3, 1, 64, dtype) == 3 * (_lib.fa_tile_shapes(dtype, 64)[0][0] // 32)
+        assert lib.fa_fwd_stamp_slots(0, 3, 100, 64, dtype) == 0
+    assert lib.fa_fwd_stamp_slots(1, 1, 64, 64, 0) == -1      # fp32 kernels carry no stamps
+    assert lib.fa_fwd_stamp_slots(1, 1, 64, 96, 1) == -1
+    assert lib.fa_fwd_stamp_slots(1, 0, 64, 64, 1) == -1
+
+
+@pytest.mark.parametrize("stamps,slots,dtype,code", [
+    (0, 1 << 20, 1, 1),                 # null stamps
+    (P + 0x600010, 1 << 20, 1, 1),      # not 32-byte aligned
+    (P + 0x600000, 3, 1, 1),            # fewer slots than waves
+    (P + 0x600000, -1, 1, 1),
+    (P + 0x300000, 1 << 20, 1, 1),      # overlaps o
+    (P + 0x600000, 1 << 20, 0, 2),      # fp32: no stamped kernel
+])
+def test_stamped_call_checks_its_buffer_before_any_hip_call(lib, stamps, slots, dtype, code):
+    args = (P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x400000, 1, 2, 1, 16, 64, 0, 0.125, dtype, None)
+    assert lib.fa_fwd_stamped(*args, stamps, slots) == code
     assert lib.fa_last_error() != b""
 
 

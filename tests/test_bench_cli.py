@@ -31,13 +31,17 @@ def test_kernel_hash_covers_sources_and_flags():
 
 
 def test_committed_shader_counters_are_read_and_go_stale_with_the_kernel(monkeypatch):
+    import json
+    with open(bench.SQ_FILE) as f:
+        stored = json.load(f)["c3_bf16_n4096_d128_causal"]["bf16"]["kernel_source_sha256"]
+    monkeypatch.setattr(bench, "kernel_hash", lambda source: stored)     # the kernel the pass measured
     c = bench.counters_for("c3_bf16_n4096_d128_causal", "bf16")
     assert c is not None
     assert 0.0 < c["mfma_busy"] <= 1.0
     assert 0.5 < c["sclk_ghz"] < 2.6
     assert c["lds_bank_conflict_rate"] >= 0.0
     assert bench.counters_for("no_such_workload", "bf16") is None
-    monkeypatch.setattr(bench, "kernel_hash", lambda source: "0" * 64)
+    monkeypatch.setattr(bench, "kernel_hash", lambda source: "0" * 64)   # the kernel changed since
     assert bench.counters_for("c3_bf16_n4096_d128_causal", "bf16") is None
     assert bench.traffic_for("c3_bf16_n4096_d128_causal", "bf16") is None
 
@@ -46,3 +50,31 @@ def test_backward_counters_are_keyed_per_kernel():
     for part in ("dq", "dkdv"):
         c = bench.counters_for("b1_bf16_bwd_n4096_d128_causal", "bwd/" + part)
         assert c is not None and 0.0 < c["mfma_busy"] <= 1.0
+
+
+def test_each_forward_workload_names_its_own_metric():
+    from flashattention_online_softmax_fwd_amd import inputs as fin
+    with open(os.path.join(ROOT, "BASELINE.json")) as f:
+        import json
+        headline = json.load(f)["metric"]
+    assert bench.metric_for(fin.WORKLOADS[fin.BENCH_WORKLOAD]) == headline
+    names = {bench.metric_for(w) for w in fin.WORKLOADS.values()}
+    assert len(names) == len(fin.WORKLOADS) - 1      # c3h and c3 differ in dtype; c5s shares c3's shape
+    assert "f16 N=2048 d=64 non-causal" in bench.metric_for(fin.WORKLOADS["c2h_f16_n2048_d64"])
+    assert "GQA 32/8" in bench.metric_for(fin.WORKLOADS["c4_bf16_gqa_n8192_d128_causal"])
+
+
+def test_oracle_leg_uses_each_dtypes_parity_bar():
+    """The fp16 bar is the bf16 one times 2^-3: an fp16 error the parity tests accept must not
+    read as a mismatch, and a bf16-sized error must read as one."""
+    import numpy as np
+
+    from oracle import tolerances
+    r = np.array([0.5, -1.0, 2.0])
+    assert tolerances.within(r + 1.0e-3, r, "f16")
+    assert not tolerances.within(r + 1.0e-2, r, "f16")
+    assert tolerances.within(r + 1.5e-2, r, "bf16")
+    assert not tolerances.within(r + 2e-5, r, "f32")
+    assert not tolerances.within(np.array([np.nan, 0, 0]), r, "bf16")
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert "tolerances.within(go, ro, w.dtype)" in src

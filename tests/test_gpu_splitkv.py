@@ -55,8 +55,10 @@ def check(x, r, atol, rtol, what):
     return float(err.max()) if err.size else 0.0
 
 
-BF16 = (1e-2, 2e-2)
-F16 = (1.25e-3, 2.5e-3)
+from oracle import tolerances  # noqa: E402
+
+BF16 = tolerances.forward_bar("bf16")
+F16 = tolerances.forward_bar("f16")
 TOL = {"bf16": BF16, "f16": F16}
 
 # B, Hq, Hkv, Nq, Nk, d, causal, splits
