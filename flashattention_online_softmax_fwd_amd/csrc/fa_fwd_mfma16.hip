@@ -24,8 +24,8 @@
 // both measured against the same, slightly stale m, so every term carries the
 // same factor and u / l is unchanged; P stays below 2^8, far from any overflow.
 // A row whose tiles so far held no finite score keeps m = -inf and adds nothing
-// (the pages' guard for a fully masked block).  l sums the E-rounded P, the
-// very weights the PV product uses.
+// (the pages' guard for a fully masked block).  l sums P in fp32, before P is
+// rounded to E for the PV product.
 //
 // Why the scores are transposed: lane L of a 32x32 MFMA output holds one column.
 // With K as the A operand that column is one query row, so the row max and sum
@@ -298,23 +298,22 @@ fwd16_kernel(const FwdParams p)
         alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
         m_ref = m_new;
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;   // nothing finite yet: P = 0
-        float ls0 = 0.f, ls1 = 0.f;
-        const ex2 one = {(E)1.f, (E)1.f};
+        // Row sums in fp32 vector adds, four chains: the pair dot product (v_dot2) would
+        // wait for the matrix products in flight on the SIMD.
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < ST; ++t)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    ex2 pair;
-                    pair[0] = (E)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e], c, -m_use));
-                    pair[1] = (E)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e + 1], c, -m_use));
-                    pb[t][u][e] = pair[0];
-                    pb[t][u][e + 1] = pair[1];
-                    if (e & 2) ls1 = Elem<E>::dot2(pair, one, ls1);
-                    else ls0 = Elem<E>::dot2(pair, one, ls0);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e], c, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * u + e + 1], c, -m_use));
+                    pb[t][u][e] = (E)p0;
+                    pb[t][u][e + 1] = (E)p1;
+                    ls[e >> 1] += p0 + p1;
                 }
-        l_run = l_run * alpha + (ls0 + ls1);
+        l_run = l_run * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
         return __builtin_amdgcn_ballot_w64(grow) != 0;
     };
 

@@ -10,14 +10,16 @@ rounded inputs; for fp32 inputs 1e-5.  It is read elementwise in allclose form,
 |x - r| <= atol + rtol * |r|, because values near zero make a pure relative bound
 meaningless and rounding O to bf16 alone costs up to 1/64 where |O| is in
 [4, 8).  The pages name no fp16 bar: fp16 takes the bf16 bar times 2^-3, the
-ratio of fp16's unit roundoff (2^-11) to bf16's (2^-8).  Every value must also
-be finite.
+ratio of fp16's unit roundoff (2^-11) to bf16's (2^-8).  fp32 adds a relative
+2^-22, two float32 roundings of the result: the absolute 1e-5 alone is finer
+than float32's own spacing for |x| >= 128 (an LSE of 6e6 is stored to 0.5).
+Every value must also be finite.
 """
 from __future__ import annotations
 
 import numpy as np
 
-FORWARD = {"bf16": (1e-2, 2e-2), "f16": (1.25e-3, 2.5e-3), "f32": (1e-5, 0.0)}
+FORWARD = {"bf16": (1e-2, 2e-2), "f16": (1.25e-3, 2.5e-3), "f32": (1e-5, 2.0 ** -22)}
 
 
 def forward_bar(dtype: str):

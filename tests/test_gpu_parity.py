@@ -9,7 +9,9 @@ can cost up to 1/64 where |O| is in [4, 8)):
     bf16 inputs:  |x - r| <= 1e-2 + 2e-2 * |r|       on O and on LSE
     fp16 inputs:  |x - r| <= 1.25e-3 + 2.5e-3 * |r|  (the bf16 bar times 2^-3, the
                   ratio of the two formats' unit roundoffs)
-    fp32 inputs:  |x - r| <= 1e-5                    on O and on LSE
+    fp32 inputs:  |x - r| <= 1e-5 + 2^-22 * |r|      on O and on LSE (the relative term is
+                  two float32 roundings: 1e-5 alone is finer than float32's spacing
+                  for |x| >= 128)
 Every O and LSE value must also be finite.
 """
 import json
