@@ -46,6 +46,8 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P] * 10 + [_I] * 6 + [ctypes.c_float, _I, _P]),
     "fa_bwd_split": (_I, [_P] * 11 + [_I] * 7 + [ctypes.c_float, _I, _P]),
     "fa_bwd_num_splits": (_I, [_I, _I, _I, _I]),
+    "fa_bwd_split_noalloc": (_I, [_P] * 10 + [_I] * 7 + [ctypes.c_float, _I, _P]),
+    "fa_bwd_noalloc_max_bytes": (ctypes.c_longlong, []),
     "fa_error_string": (ctypes.c_char_p, [_I]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (_I, []),
@@ -128,6 +130,16 @@ def fa_bwd_split(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits,
                  scale, dtype, stream):
     return load().fa_bwd_split(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits, B, Hq, Hkv, N, d,
                                causal, scale, dtype, stream)
+
+
+def fa_bwd_split_noalloc(q, k, v, o, lse, dout, dq, dk, dv, delta, num_splits, B, Hq, Hkv, N, d, causal, scale,
+                         dtype, stream):
+    return load().fa_bwd_split_noalloc(q, k, v, o, lse, dout, dq, dk, dv, delta, num_splits, B, Hq, Hkv, N, d,
+                                       causal, scale, dtype, stream)
+
+
+def fa_bwd_noalloc_max_bytes():
+    return load().fa_bwd_noalloc_max_bytes()
 
 
 def fa_bwd_num_splits(B, Hq, Hkv, N):

@@ -30,6 +30,8 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace fa {
 namespace bwd {
 constexpr float kLog2e = 1.4426950408889634f;
@@ -564,6 +566,49 @@ FA_BWD_INSTANTIATE(__bf16, 128)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(_Float16, 128)
 FA_BWD_INSTANTIATE(_Float16, 64)
+
+// The workspace of the allocation-free split backward (fa_bwd_split_noalloc): room for
+// the fp32 dK/dV partials [2][splits][B][Hkv][N][d] of calls up to kBwdScratchBytes.
+// Each GPU holds its own copy from the moment the library's code is loaded on it
+// until the process ends.  Every dK/dV workgroup writes its whole share of it, so
+// nothing has to be cleared between calls; calls that overlap on one GPU race.
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
+// The lookup below is compiled in both passes: the device pass must see that host code
+// takes the array's address, or it drops the array as unused and the runtime then has
+// no device symbol behind the name.
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+}  // namespace
+
+hipError_t bwd_scratch(hipStream_t stream, float** ptr)
+{
+    int dev = 0;
+    hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    // Once per device, with that device current: in host code the array's name is only a
+    // stand-in, so its device address is looked up and kept.
+    std::call_once(g_scratch_once[dev], [dev]() {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        if (e == hipSuccess) e = hipGetSymbolAddress((void**)&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e == hipSuccess && !g_scratch_ptr[dev]) e = hipErrorInvalidSymbol;
+        g_scratch_err[dev] = e;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 namespace {

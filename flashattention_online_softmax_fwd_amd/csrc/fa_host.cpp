@@ -315,9 +315,11 @@ int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, in
     return FA_OK;
 }
 
+// static_scratch: the dK/dV partials go to the library's static workspace (fa::bwd_scratch)
+// instead of dkv_part, which must then be null.
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
             void* dq, void* dk, void* dv, float* delta, float* dkv_part, int num_splits, int B, int Hq, int Hkv,
-            int N, int d, int causal, float scale, int dtype, void* stream)
+            int N, int d, int causal, float scale, int dtype, void* stream, bool static_scratch = false)
 {
     g_last_error.clear();
     if (!known_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype " + std::to_string(dtype));
@@ -328,7 +330,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
         return fail(FA_ERR_INVALID_ARG, "num_splits must be in 1.." + std::to_string(kMaxBwdSplits));
     if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "d must be 64 or 128");
     if (B == 0 || N == 0) return FA_OK;
-    if (num_splits > 1 && !dkv_part) return fail(FA_ERR_INVALID_ARG, "dkv_part is required when num_splits > 1");
+    if (num_splits > 1 && !dkv_part && !static_scratch)
+        return fail(FA_ERR_INVALID_ARG, "dkv_part is required when num_splits > 1");
     if (num_splits > 1 && reinterpret_cast<uintptr_t>(dkv_part) % 16 != 0)
         return fail(FA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
 
@@ -347,7 +350,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     const uint64_t in_n[6] = {qbytes, kvbytes, kvbytes, qbytes, lbytes, qbytes};
     void* out[5] = {dq, dk, dv, delta, dkv_part};
     const uint64_t out_n[5] = {qbytes, kvbytes, kvbytes, lbytes, pbytes};
-    const int nout = num_splits > 1 ? 5 : 4;
+    const int nout = num_splits > 1 && !static_scratch ? 5 : 4;
     for (int a = 0; a < nout; ++a) {
         for (int i = 0; i < 6; ++i)
             if (overlaps(out[a], out_n[a], in[i], in_n[i]))
@@ -383,6 +386,15 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     p.xcd_map = 0;
     p.splits = num_splits;
     p.dkv_part = num_splits > 1 ? dkv_part : nullptr;
+    if (static_scratch && num_splits > 1) {
+        if (pbytes > fa::kBwdScratchBytes)
+            return fail(FA_ERR_UNSUPPORTED, "the dK/dV partials (" + std::to_string(pbytes) +
+                                                " bytes) exceed the static workspace of " +
+                                                std::to_string(fa::kBwdScratchBytes) + " bytes");
+        const hipError_t serr = fa::bwd_scratch(static_cast<hipStream_t>(stream), &p.dkv_part);
+        if (serr != hipSuccess)
+            return fail(FA_ERR_HIP, std::string("static workspace: ") + hipGetErrorString(serr));
+    }
     const hipError_t err = fa::launch_bwd(p, d, dtype, causal, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
     return FA_OK;
@@ -411,6 +423,19 @@ int fa_bwd_split(const void* q, const void* k, const void* v, const void* o, con
 {
     return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, dkv_part, num_splits, B, Hq, Hkv, N, d, causal, scale,
                    dtype, stream);
+}
+
+int fa_bwd_split_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int num_splits, int B,
+                         int Hq, int Hkv, int N, int d, int causal, float scale, int dtype, void* stream)
+{
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, nullptr, num_splits, B, Hq, Hkv, N, d, causal, scale,
+                   dtype, stream, true);
+}
+
+long long fa_bwd_noalloc_max_bytes(void)
+{
+    return (long long)fa::kBwdScratchBytes;
 }
 
 int fa_bwd_num_splits(int B, int Hq, int Hkv, int N)
@@ -543,7 +568,7 @@ const char* fa_last_error(void)
 
 int fa_abi_version(void)
 {
-    return 6;
+    return 7;
 }
 
 }  // extern "C"

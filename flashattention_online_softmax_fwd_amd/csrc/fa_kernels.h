@@ -87,6 +87,12 @@ struct BwdParams {
 // dtype FA_DTYPE_BF16 or FA_DTYPE_F16.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, int causal, hipStream_t stream);
 
+// The library's own dK/dV partial workspace for fa_bwd_split_noalloc: a static device
+// array of kBwdScratchBytes on each GPU.  *ptr receives its device address on the
+// stream's device (looked up once per device).
+constexpr unsigned long long kBwdScratchBytes = 128ULL << 20;
+hipError_t bwd_scratch(hipStream_t stream, float** ptr);
+
 // Row softmax: y [rows][cols] = softmax of each row of x, lse [rows] (optional).
 struct SoftmaxParams {
     const void* x;

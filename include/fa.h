@@ -38,7 +38,8 @@
  *
  * Ownership: every buffer belongs to the caller and is device memory of the
  * device the stream belongs to.  The library never allocates, frees or keeps a
- * pointer past the call; the only workspace it takes is fa_bwd_split's dkv_part.
+ * pointer past the call; the only workspace it takes is fa_bwd_split's dkv_part
+ * (fa_bwd_split_noalloc uses a static array of the library in its place).
  * q, k and v are only read; o and lse must not overlap the inputs or each other.
  * Every pointer must be 16-byte aligned.
  *
@@ -289,13 +290,38 @@ int fa_bwd_split(const void* q, const void* k, const void* v, const void* o, con
  * key tiles alone reach that, at most 8), or -1 for a bad size. */
 int fa_bwd_num_splits(int B, int Hq, int Hkv, int N);
 
+/*
+ * fa_bwd_split_noalloc: fa_bwd_split without the caller's workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The fp32 dK/dV partials go to a static device
+ * array of the library instead of dkv_part: fa_bwd_noalloc_max_bytes() bytes
+ * (128 MiB), one copy per GPU, held from the library's first use on that GPU until
+ * the process ends.  The call allocates nothing.
+ *
+ *   num_splits  1..8 as for fa_bwd_split; the partials take
+ *               2 * num_splits * B * Hkv * N * d * 4 bytes (none when num_splits is 1);
+ *               more than the array holds returns FA_ERR_UNSUPPORTED, nothing enqueued
+ *   other arguments, ownership, alignment and errors: as for fa_bwd_split.  The results
+ *   are bitwise fa_bwd_split's for the same arguments.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.  Nothing
+ * in it needs clearing: each call overwrites the part it reads.
+ */
+int fa_bwd_split_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int num_splits,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale, int dtype,
+                         void* stream);
+
+/* Bytes of the static workspace of fa_bwd_split_noalloc. */
+long long fa_bwd_noalloc_max_bytes(void);
+
 /* Static text for a return code. */
 const char* fa_error_string(int code);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

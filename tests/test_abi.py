@@ -32,7 +32,8 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == {"fa_fwd", "fa_fwd_tiled", "fa_tile_shapes", "fa_error_string",
                           "fa_last_error", "fa_abi_version", "fa_fwd_splitkv", "fa_merge",
                           "fa_split_chunk", "fa_splitkv_num_splits", "fa_softmax", "fa_bwd", "fa_bwd_split",
-                          "fa_bwd_num_splits", "fa_fwd_stamped", "fa_fwd_stamp_slots", "fa_wall_clock_khz"}
+                          "fa_bwd_num_splits", "fa_fwd_stamped", "fa_fwd_stamp_slots", "fa_wall_clock_khz",
+                          "fa_bwd_split_noalloc", "fa_bwd_noalloc_max_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(PKG, "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)", out))
@@ -65,7 +66,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_version_and_error_strings(lib):
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
     assert lib.fa_error_string(0) == b"ok"
     assert lib.fa_error_string(1) == b"invalid argument"
     assert lib.fa_error_string(2) == b"unsupported request"
@@ -308,3 +309,37 @@ def test_head_size_limit_leaves_room_for_the_last_tile(lib):
     assert b"2 GiB" in lib.fa_last_error()
     assert call_split(lib, Nq=1, Nk=n_over, d=128, Hq=1, Hkv=1, causal=0) == 2
     assert call_bwd(lib, N=n_over, d=128, Hq=1, Hkv=1) == 2
+
+
+def call_bwd_noalloc(lib, splits=2, **kw):
+    a = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000, do=P + 0x500000,
+             dq=P + 0x600000, dk=P + 0x700000, dv=P + 0x800000, delta=P + 0x900000, B=1, Hq=2, Hkv=1, N=300,
+             d=64, causal=1, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return lib.fa_bwd_split_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                    a["delta"], splits, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                    a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0), 1), (dict(splits=9), 1), (dict(q=0), 1), (dict(dq=P + 0x500000), 1),
+    (dict(dtype=0), 2), (dict(d=96), 2), (dict(Hq=3, Hkv=2), 1),
+])
+def test_bwd_noalloc_rejects_bad_arguments_before_any_hip_call(lib, kw, code):
+    assert call_bwd_noalloc(lib, **kw) == code
+    assert lib.fa_last_error() != b""
+
+
+def test_bwd_noalloc_refuses_partials_beyond_its_static_workspace(lib):
+    """2 * splits * B * Hkv * N * d * 4 bytes must fit the static array; a larger call is
+    refused on the host, before any HIP call, with the sizes in the message."""
+    cap = lib.fa_bwd_noalloc_max_bytes()
+    assert cap == 128 << 20
+    # 2 * 8 * 1 * 8 * 4096 * 128 * 4 = 256 MiB > 128 MiB (pointers spaced so nothing overlaps)
+    big = dict(q=P, k=P + (1 << 32), v=P + (2 << 32), o=P + (3 << 32), lse=P + (4 << 32), do=P + (5 << 32),
+               dq=P + (6 << 32), dk=P + (7 << 32), dv=P + (8 << 32), delta=P + (9 << 32),
+               B=1, Hq=8, Hkv=8, N=4096, d=128)
+    assert call_bwd_noalloc(lib, splits=8, **big) == 2
+    assert b"static workspace" in lib.fa_last_error()
+    z = dict(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0)
+    assert call_bwd_noalloc(lib, splits=8, B=0, **z) == 0          # empty: nothing to do

@@ -79,3 +79,15 @@ def test_backward_barriers_wait_for_lds_dma_and_nothing_spills(bwd_asm):
         assert not any(x.startswith(("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")) for x in ins), name
         assert not any(x.startswith("scratch_") for x in ins), name
     assert found == 16      # dq and dk/dv, bf16 and fp16, d 64 and 128, causal or not
+
+
+def test_static_workspace_is_a_device_symbol(bwd_asm):
+    """The allocation-free backward looks up its static workspace by name at run time.  The
+    device pass must emit the array as a global symbol of its full size: if the device pass
+    does not see host code take its address (for instance because that code is compiled
+    for the host only), it drops the unused array, and the runtime's lookup of the name the
+    host registers then aborts the process."""
+    m = re.search(r"^\s*\.globl\s+(\S*scratch\S*)\s*$", bwd_asm, re.M)
+    assert m, "no global device symbol for the static workspace"
+    size = re.search(r"^\s*\.size\s+%s,\s*(\d+)" % re.escape(m.group(1)), bwd_asm, re.M)
+    assert size and int(size.group(1)) == 128 << 20
