@@ -60,6 +60,35 @@ class LibraryNotBuilt(ImportError):
     pass
 
 
+class TwoHipRuntimes(RuntimeError):
+    pass
+
+
+def hip_runtimes_mapped():
+    """Distinct HIP runtime files (libamdhip64*) mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
+def check_one_hip_runtime():
+    """Raise TwoHipRuntimes when more than one HIP runtime is mapped.
+
+    torch's libraries ask for ``libamdhip64.so`` and find their own copy next to them;
+    libfa asks for ``libamdhip64.so.7``, the soname of that copy.  Loaded after torch,
+    libfa therefore binds to torch's runtime.  Loaded first, it maps the system
+    runtime, and torch then maps its own beside it: torch's stream handles are then
+    foreign to the runtime libfa launches on, and the first launch can abort the
+    process.  This turns that state into an error before any launch.
+    """
+    mapped = hip_runtimes_mapped()
+    if len(mapped) > 1:
+        raise TwoHipRuntimes("two HIP runtimes are mapped into this process (%s): load libfa only after "
+                             "torch, through this module" % ", ".join(mapped))
+
+
 def load():
     """Load libfa.so once; raise LibraryNotBuilt if it is missing."""
     global _lib
@@ -69,6 +98,7 @@ def load():
                 "libfa.so is not built (%s); run `python -c 'import __graft_entry__ as g; g.build()'`"
                 % LIB_PATH)
         lib = ctypes.CDLL(LIB_PATH)
+        check_one_hip_runtime()
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype = res

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -343,3 +344,27 @@ def test_bwd_noalloc_refuses_partials_beyond_its_static_workspace(lib):
     assert b"static workspace" in lib.fa_last_error()
     z = dict(q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0)
     assert call_bwd_noalloc(lib, splits=8, B=0, **z) == 0          # empty: nothing to do
+
+
+def _fresh(code):
+    return subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+
+
+def test_binding_maps_one_hip_runtime():
+    """Through the binding (torch first) libfa binds to torch's HIP runtime: one is mapped."""
+    r = _fresh("from flashattention_online_softmax_fwd_amd import _lib\n_lib.load()\n"
+               "print(len(_lib.hip_runtimes_mapped()))")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1"
+
+
+def test_loading_libfa_before_torch_is_refused_before_any_launch():
+    """libfa loaded ahead of torch maps the system HIP runtime and torch then maps its own:
+    the binding refuses to run in that state instead of launching into it."""
+    r = _fresh("import ctypes\nctypes.CDLL('flashattention_online_softmax_fwd_amd/libfa.so')\n"
+               "from flashattention_online_softmax_fwd_amd import _lib\n"
+               "print(len(_lib.hip_runtimes_mapped()))\n"
+               "try:\n    _lib.load()\nexcept _lib.TwoHipRuntimes as e:\n    print('refused', e)\n")
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.splitlines()
+    assert lines[0] == "2" and lines[1].startswith("refused")
