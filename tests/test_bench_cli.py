@@ -46,8 +46,13 @@ def test_committed_shader_counters_are_read_and_go_stale_with_the_kernel(monkeyp
     assert bench.traffic_for("c3_bf16_n4096_d128_causal", "bf16") is None
 
 
-def test_backward_counters_are_keyed_per_kernel():
+def test_backward_counters_are_keyed_per_kernel(monkeypatch):
+    import json
+    with open(bench.SQ_FILE) as f:
+        table = json.load(f)["b1_bf16_bwd_n4096_d128_causal"]
     for part in ("dq", "dkdv"):
+        stored = table["bwd/" + part]["kernel_source_sha256"]
+        monkeypatch.setattr(bench, "kernel_hash", lambda source: stored)   # the kernel the pass measured
         c = bench.counters_for("b1_bf16_bwd_n4096_d128_causal", "bwd/" + part)
         assert c is not None and 0.0 < c["mfma_busy"] <= 1.0
 
