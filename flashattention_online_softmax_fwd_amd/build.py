@@ -19,7 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_host.cpp", "fa_fwd_mfma16.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_softmax.hip", "fa_bwd_mfma16.hip"]
+SOURCES = ["fa_host.cpp", "fa_fwd_mfma16.hip", "fa_fwd_w64.hip", "fa_fwd_f32.hip", "fa_merge.hip", "fa_softmax.hip",
+           "fa_bwd_mfma16.hip"]
+# Sources generated before compiling: the key loop of fa_fwd_w64.hip (gfx950 assembly).
+GENERATORS = [os.path.join(CSRC, "gen_fwd_kloop.py")]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
@@ -57,7 +60,16 @@ def _compile(src: str) -> str:
     return obj
 
 
+def generate() -> None:
+    """Regenerate the generated sources (fa_fwd_kloop.inc) from their generators."""
+    for gen in GENERATORS:
+        r = subprocess.run([sys.executable, gen], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("generating from %s failed:\n%s" % (gen, r.stderr))
+
+
 def build(verbose: bool = False) -> str:
+    generate()
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))

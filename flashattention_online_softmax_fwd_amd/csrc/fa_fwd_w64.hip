@@ -1,0 +1,231 @@
+// fa_fwd_w64.hip -- FlashAttention forward for gfx950 (CDNA4, MI355X), 16-bit inputs
+// (bf16 or fp16), head dimension 128: 64 query rows per wave, one wave per SIMD.
+//
+// Same method and the same per-row arithmetic as fwd16_kernel (fa_fwd_mfma16.hip): the
+// online softmax of the pages in base 2 (mbrenndoerfer.com "Online Softmax Computation",
+// its update equations; spicyshark.co online-softmax lesson, "The idea", "From softmax to
+// attention" and "The implementation"), query blocks outer and key blocks inner (kbwen.com
+// FlashAttention feed, "More than two blocks"), with the reference m moved only when the
+// row maximum has grown by more than 2^8 (l and O share the stale reference, so u / l is
+// unchanged), and the guard for rows with no finite score yet (0 as the exp reference).
+// P is summed into l in fp32 before it is rounded to the element type for the PV product.
+//
+// What differs is the shape of the work.  A workgroup of 2 waves owns 128 query rows; each
+// wave owns 64 of them as two 32-row blocks, so every K or V operand read from LDS feeds two
+// matrix products (half the LDS reads per flop of a 32-row wave).  Two workgroups share a
+// CU: one wave per SIMD.  The output accumulators (128 per lane) stay in AGPRs for the whole
+// key walk, so the register file holds Q, two score buffers and two weight buffers beside
+// them.  The key walk runs in 32-key halves of the 64-key LDS tiles; in half h a wave issues
+// the score products of half h+1 and the value products of half h-1 while its vector unit
+// runs the softmax of half h.  That schedule is written out as assembly by gen_fwd_kloop.py
+// (fa_fwd_kloop.inc): the compiler would copy the accumulators out of the AGPRs for the rare
+// rescale and would not keep the three streams interleaved.  This file computes the
+// addresses and hands them to that assembly; the assembly loads Q, walks the tiles and
+// stores O and LSE.
+//
+// LDS (64 KiB per workgroup): K tiles at +0 and +16 KiB, V tiles at +32 and +48 KiB, each
+// [64 keys][128 dims] with 16-byte chunks XOR-swizzled per row (the layout of
+// fa_fwd_mfma16.hip), filled by buffer_load_dwordx4 ... lds.  Rows past N read as zero and
+// rows of O and LSE past N are not written: every buffer range ends at the head's last row.
+#include "fa_kernels.h"
+#include "fa_mfma16_common.h"
+#include "fa_fwd_kloop.inc"
+
+#include <float.h>
+#include <stdint.h>
+
+namespace fa {
+
+#define FA_W64_CLOBBERS                                                                                   \
+    "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", "v10", "v11", "v12", "v13", "v14", "v15",   \
+    "v16", "v17", "v18", "v19", "v20", "v21", "v22", "v23", "v24", "v25", "v26", "v27", "v28", "v29", "v30", \
+    "v31", "v32", "v33", "v34", "v35", "v36", "v37", "v38", "v39", "v40", "v41", "v42", "v43", "v44", "v45", \
+    "v46", "v47", "v48", "v49", "v50", "v51", "v52", "v53", "v54", "v55", "v56", "v57", "v58", "v59", "v60", \
+    "v61", "v62", "v63", "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", \
+    "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", \
+    "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104",   \
+    "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117",  \
+    "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127", "v128", "v129", "v130",  \
+    "v131", "v132", "v133", "v134", "v135", "v136", "v137", "v138", "v139", "v140", "v141", "v142", "v143",  \
+    "v144", "v145", "v146", "v147", "v148", "v149", "v150", "v151", "v152", "v153", "v154", "v155", "v156",  \
+    "v157", "v158", "v159", "v160", "v161", "v162", "v163", "v164", "v165", "v166", "v167", "v168", "v169",  \
+    "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182",  \
+    "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195",  \
+    "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208",  \
+    "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", "v220", "v221",  \
+    "v222", "v223",                                                                                           \
+    "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15",   \
+    "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", \
+    "a31", "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", \
+    "a46", "a47", "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", \
+    "a61", "a62", "a63", "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", \
+    "a76", "a77", "a78", "a79", "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", \
+    "a91", "a92", "a93", "a94", "a95", "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104",   \
+    "a105", "a106", "a107", "a108", "a109", "a110", "a111", "a112", "a113", "a114", "a115", "a116", "a117",  \
+    "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "vcc", "m0", "scc",       \
+    "memory"
+
+template <typename E, bool CAUSAL>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd_w64_kernel(const FwdParams p)
+{
+    constexpr int D = 128;
+    constexpr int ROWB = D * 2;
+    // K0, K1, V0, V1.  Aligned to 32 KiB: the walk switches buffers by flipping bit 14 of
+    // the addresses.
+    __shared__ __attribute__((aligned(32768))) char lds[65536];
+
+    const int N = p.N;
+    const int units = p.B * p.Hq;
+    const int nqt = p.n_qtiles;
+    const int bid = blockIdx.x;
+    int bh, qt;
+    if (p.xcd_map) {
+        int t;
+        xcd_order(bid, units, nqt, bh, t);
+        qt = CAUSAL ? nqt - 1 - t : t;   // longest first
+    } else {
+        bh = bid % units;
+        qt = CAUSAL ? nqt - 1 - bid / units : bid / units;
+    }
+    const int b = bh / p.Hq;
+    const int hk = (bh - b * p.Hq) / p.group;
+    const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
+    const char* Vh = (const char*)p.v + (size_t)(b * p.Hkv + hk) * N * ROWB;
+    const char* Qh = (const char*)p.q + (size_t)bh * N * ROWB;
+    char* Oh = (char*)p.o + (size_t)bh * N * ROWB;
+    float* Lh = p.lse + (size_t)bh * N;
+    const int range = N * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)Oh, (short)0, range, 0x00020000);
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)Lh, (short)0, N * 4, 0x00020000);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    unsigned long long real0 = 0, cyc0 = 0;
+    if (p.stamps) {
+        real0 = __builtin_amdgcn_s_memrealtime();
+        cyc0 = __builtin_amdgcn_s_memtime();
+    }
+
+    const int q0 = qt * 128;
+    const int row0 = q0 + 64 * wave;                    // the wave's first query row
+    const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
+    const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
+    const int loff = (row0 + l32) * 4;
+    const unsigned ldsb = (unsigned)(uintptr_t)(FA_LDS char*)lds;
+
+    // K operand: row l32 of the 32-key block, logical chunk 2kk + hi (buffer K0 to start).
+    const int kx = swz<D>(l32);
+    int koff[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) koff[kk] = (int)ldsb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
+    // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
+    // step and dims 32dt + 16(G&1) + 4s ..; buffer V1 to start (the walk flips to V0 first).
+    const int G = lane >> 4;
+    const int jj = (lane >> 2) & 3;
+    const int ss = lane & 3;
+    int voff[8];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 8 * r + 4 * (G >> 1) + jj;
+        const int w = swz<D>(row);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
+            voff[4 * r + dt] = (int)ldsb + 49152 + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+        }
+    }
+    // Tile loads: slice ii = wave + 2i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
+    // lane's 16 bytes are row 4ii + lane/16, physical chunk lane%16, i.e. logical chunk
+    // (lane%16) ^ swz(row).  Only ii's low two bits enter the swizzle: two patterns (i even, odd).
+    int dma[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int row = 4 * (wave + 2 * e) + (lane >> 4);
+        dma[e] = 1024 * wave + (lane >> 4) * ROWB + 16 * ((lane & 15) ^ swz<D>(row));
+    }
+    const int dmask = l32 - 4 * hi;   // causal: key 8(r>>2) + (r&3) + 4hi of a diagonal half visible iff <= row l32
+    const int hi4 = 4 * hi;
+
+    // Key tiles of 64 for the workgroup; the last one this wave's rows need.
+    const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
+    const int nt = (kv_end + 63) / 64;
+    const int last = CAUSAL ? min(nt - 1, q0 / 64 + wave) : nt - 1;
+    const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
+    const int limA = valid_last - 1;
+    const int limB = valid_last - 33;
+    // A negative scale is folded into Q's sign; a zero scale becomes the smallest normal.
+    const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
+    const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
+
+    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 32768 + 1024 * wave;
+    unsigned soff, kit, cnt;
+    unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
+    int dlim;
+#define FA_W64_ASM(TEXT)                                                                                   \
+    asm volatile(TEXT                                                                                      \
+                 : [koff0] "+v"(koff[0]), [koff1] "+v"(koff[1]), [koff2] "+v"(koff[2]), [koff3] "+v"(koff[3]),  \
+                   [koff4] "+v"(koff[4]), [koff5] "+v"(koff[5]), [koff6] "+v"(koff[6]), [koff7] "+v"(koff[7]),  \
+                   [voff0] "+v"(voff[0]), [voff1] "+v"(voff[1]), [voff2] "+v"(voff[2]), [voff3] "+v"(voff[3]),  \
+                   [voff4] "+v"(voff[4]), [voff5] "+v"(voff[5]), [voff6] "+v"(voff[6]), [voff7] "+v"(voff[7]),  \
+                   [ksrc] "+s"(ksrc), [kdst] "+s"(kdst), [vsrc] "+s"(vsrc), [vdst] "+s"(vdst),                   \
+                   [soff] "=&s"(soff), [kit] "=&s"(kit), [cnt] "=&s"(cnt),                                      \
+                   [g00] "=&s"(g00), [g01] "=&s"(g01), [g10] "=&s"(g10), [g11] "=&s"(g11), [ga0] "=&s"(ga0),    \
+                   [ga1] "=&s"(ga1), [mk1] "=&s"(mk1), [mk2] "=&s"(mk2), [mk3] "=&s"(mk3), [mk4] "=&s"(mk4),    \
+                   [mk5] "=&s"(mk5), [mk6] "=&s"(mk6), [mk7] "=&s"(mk7), [dlim] "=&v"(dlim)                     \
+                 : [dma0] "v"(dma[0]), [dma1] "v"(dma[1]), [qoff] "v"(qoff), [ooff] "v"(ooff), [loff] "v"(loff),  \
+                   [dmask] "v"(dmask), [hi4] "v"(hi4), [krs] "s"(krs), [vrs] "s"(vrs), [qrs] "s"(qrs),             \
+                   [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
+                   [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip)                                                 \
+                 : FA_W64_CLOBBERS)
+    if constexpr (__is_same(E, __bf16)) {
+        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL);
+        else FA_W64_ASM(FA_KLOOP_BF16_FULL);
+    } else {
+        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL);
+        else FA_W64_ASM(FA_KLOOP_F16_FULL);
+    }
+#undef FA_W64_ASM
+
+    if (p.stamps && lane == 0) {
+        const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
+        const unsigned long long real1 = __builtin_amdgcn_s_memrealtime();
+        typedef __attribute__((ext_vector_type(4))) unsigned long long u64x4;
+        *(u64x4*)(p.stamps + ((size_t)bid * 2 + wave) * 4) = u64x4{real0, real1, cyc0, cyc1};
+    }
+}
+
+template __global__ void fwd_w64_kernel<__bf16, false>(const FwdParams);
+template __global__ void fwd_w64_kernel<__bf16, true>(const FwdParams);
+template __global__ void fwd_w64_kernel<_Float16, false>(const FwdParams);
+template __global__ void fwd_w64_kernel<_Float16, true>(const FwdParams);
+
+#if !defined(__HIP_DEVICE_COMPILE__)
+namespace {
+
+template <typename E, bool CAUSAL>
+hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
+{
+    const long long units = (long long)p.B * p.Hq;
+    FwdParams args = p;
+    args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
+    void* kargs[] = {&args};
+    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL>, dim3((unsigned)(units * p.n_qtiles)), dim3(128),
+                           kargs, 0, stream);
+}
+
+}  // namespace
+
+const KernelEntry kBf16W64Kernels[] = {{1, 128, 128, 64, 0, &launch_w64<__bf16, false>, 2},
+                                       {1, 128, 128, 64, 1, &launch_w64<__bf16, true>, 2}};
+const KernelEntry kF16W64Kernels[] = {{2, 128, 128, 64, 0, &launch_w64<_Float16, false>, 2},
+                                      {2, 128, 128, 64, 1, &launch_w64<_Float16, true>, 2}};
+#endif
+
+}  // namespace fa

@@ -48,6 +48,13 @@ const fa::KernelEntry* table_for(int dtype, int* n)
 
 const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n)
 {
+    // 16-bit inputs at d = 128: the 64-rows-per-wave kernel serves the default 128 x 64 tile
+    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128 &&
+        ((block_m == 0 && block_n == 0) || (block_m == 128 && block_n == 64))) {
+        const fa::KernelEntry* w = dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels;
+        for (int i = 0; i < fa::kNumW64Kernels; ++i)
+            if (w[i].causal == causal) return &w[i];
+    }
     int n = 0;
     const fa::KernelEntry* table = table_for(dtype, &n);
     for (int i = 0; i < n; ++i) {
@@ -132,7 +139,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const uint64_t grid = (uint64_t)B * (uint64_t)Hq * ntiles;
     if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
     if (stamps) {
-        const uint64_t slots = grid * (uint64_t)(e->block_m / 32);   // one per wave of 32 rows
+        const uint64_t slots = grid * (uint64_t)(e->waves ? e->waves : e->block_m / 32);   // one per wave
         if (stamp_slots < 0 || (uint64_t)stamp_slots < slots)
             return fail(FA_ERR_INVALID_ARG, "stamps holds fewer slots than the launch has waves");
         if (overlaps(stamps, slots * 32, q, qbytes) || overlaps(stamps, slots * 32, k, kvbytes) ||
@@ -477,7 +484,8 @@ long long fa_fwd_stamp_slots(int B, int Hq, int N, int d, int dtype)
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return -1;
     const fa::KernelEntry* e = find_kernel(dtype, d, 0, 0, 0);
     if (!e) return -1;
-    return (long long)B * Hq * (((long long)N + e->block_m - 1) / e->block_m) * (e->block_m / 32);
+    return (long long)B * Hq * (((long long)N + e->block_m - 1) / e->block_m) *
+           (e->waves ? e->waves : e->block_m / 32);
 }
 
 int fa_wall_clock_khz(int device)

@@ -37,6 +37,7 @@ struct KernelEntry {
     int block_n;
     int causal;
     Launcher launch;
+    int waves;      // waves per workgroup; 0: block_m / 32 (one 32-row block per wave)
 };
 
 // Tables defined by the kernel translation units.
@@ -46,6 +47,11 @@ extern const KernelEntry kF16Kernels[];
 extern const int kNumF16Kernels;
 extern const KernelEntry kF32Kernels[];
 extern const int kNumF32Kernels;
+// The 64-rows-per-wave forward (fa_fwd_w64.hip): d = 128, 128 x 64 tiles, the default for
+// 16-bit inputs at d = 128.
+extern const KernelEntry kBf16W64Kernels[];
+extern const KernelEntry kF16W64Kernels[];
+constexpr int kNumW64Kernels = 2;
 // Split-KV partial-state kernels (16-bit inputs, float partial outputs).
 extern const KernelEntry kBf16SplitKernels[];
 extern const int kNumBf16SplitKernels;

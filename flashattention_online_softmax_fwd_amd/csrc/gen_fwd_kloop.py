@@ -1,0 +1,799 @@
+#!/usr/bin/env python3
+"""Generates fa_fwd_kloop.inc: the key loop of the 64-rows-per-wave forward as gfx950 assembly.
+
+The forward of fa_fwd_w64.hip hands one wave 64 query rows (two 32-row blocks, rb 0 and 1) at
+one wave per SIMD, so each K or V operand read from LDS feeds two matrix products.  The
+whole per-workgroup computation after the setup is one inline-assembly statement built
+here: the Q loads, the pipelined walk over 64-key tiles, the rare rescale of the output
+accumulators, and the stores of O and LSE.  Writing it out lets the output accumulators
+stay in AGPRs for the whole walk (only the rare rescale touches them outside the matrix
+products) and lets every matrix product sit between the vector work of the softmax and
+the LDS reads of the next operands.
+
+The method is the pages' online softmax in base 2 with the kernel's lazy reference (see
+fa_fwd_w64.hip).  Per 32-key half-tile h of a wave:
+    S(h+1) = K Q^T        (the next half's scores, 16 products)
+    O     += V^T P(h-1)   (the previous half's weighted values, 16 products)
+    softmax(h) on the scores of this half: row max, lazy reference move, P = exp2(S c - m),
+                          row sums, P rounded to the element type
+The scores of half h+1 are therefore computed while half h's exponentials run, and the
+values of half h-1 are added while half h's row maxima are formed.
+
+Register plan (fixed, named by the clobber list of the statement):
+    v0..v63     Q, rb * 32 + kk * 4 (kk = 16-dim step)
+    v64..v127   S, two buffers of two row blocks
+    v128..v159  P, two buffers, [rb][ks] (ks = 16-key step)
+    v160..v175  K operand staging (4), v176..v191 V operand staging (4)
+    v192..v199  m, l, alpha[parity][rb]
+    v200..v223  temporaries
+    a0..a127    O, [rb][db] (db = 32-dim block)
+Everything the hardware does not interlock is spaced by this generator: it tracks the
+producer of every register and inserts s_nop for the wait states the CDNA3/CDNA4 hazard
+rules require (matrix result -> vector use, vector result -> matrix operand,
+transcendental -> use, lane-mask write -> use, M0 write -> LDS DMA), and s_waitcnt
+lgkmcnt for LDS reads still in flight when their destination is used.
+
+Run:  python gen_fwd_kloop.py      (writes fa_fwd_kloop.inc next to this file)
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "fa_fwd_kloop.inc")
+
+NEG_INF_BITS = "0xff800000"
+
+# ---------------------------------------------------------------- registers
+
+def vr(i):
+    return "v%d" % i
+
+
+def vrange(a, n):
+    return "v[%d:%d]" % (a, a + n - 1)
+
+
+def Qr(rb, kk):
+    return 32 * rb + 4 * kk
+
+
+def Sr(buf, rb):
+    return 64 + 32 * buf + 16 * rb
+
+
+def Pr(buf, rb, ks):
+    return 128 + 16 * buf + 8 * rb + 4 * ks
+
+
+def KST(i):
+    return 160 + 4 * i
+
+
+def VST(i):
+    return 176 + 4 * i
+
+
+def Mr(rb):
+    return 192 + rb
+
+
+def Lr(rb):
+    return 194 + rb
+
+
+def ALr(par, rb):
+    return 196 + 2 * par + rb
+
+
+TMP0 = 200           # v200..v223
+NTMP = 24
+NEGINF = 223         # holds -inf for lane-mask selects
+NVCLOB = 224         # v0..v223 clobbered
+
+
+def Or(rb, db):
+    return 64 * rb + 16 * db
+
+
+# ---------------------------------------------------------------- instructions
+
+class Ins:
+    """One instruction with the registers it reads and writes (for the hazard and
+    waitcnt passes).  kind: mfma, valu, trans, perm, cmps (VALU writing an SGPR mask),
+    accr, accw, salu, m0 (SALU writing M0), lds (LDS read), dma (LDS DMA load),
+    vload, vstore, barrier, wait, nop, branch, label."""
+
+    __slots__ = ("text", "kind", "defs", "uses", "srcc")
+
+    def __init__(self, text, kind, defs=(), uses=(), srcc=None):
+        self.text = text
+        self.kind = kind
+        self.defs = tuple(defs)
+        self.uses = tuple(uses)
+        self.srcc = srcc
+
+
+def regs(a, n, prefix="v"):
+    return ["%s%d" % (prefix, a + i) for i in range(n)]
+
+
+class Skip:
+    """A forward branch over ``body`` when the 64-bit SGPR operand ``flag`` is zero."""
+
+    def __init__(self, flag, body, label):
+        self.flag = flag
+        self.body = body
+        self.label = label
+
+
+class Loop:
+    """``body`` repeated while the SGPR operand ``counter`` (decremented at the end) is
+    non-zero; entered only when it is non-zero."""
+
+    def __init__(self, counter, body, label):
+        self.counter = counter
+        self.body = body
+        self.label = label
+
+
+class Cond:
+    """``body`` run only when SCC (set by ``test``, a list of SALU texts) is 1."""
+
+    def __init__(self, test, body, label):
+        self.test = test
+        self.body = body
+        self.label = label
+
+
+# ---------------------------------------------------------------- hazard rules
+
+MFMA_WAIT = 20    # matrix result -> any other access of that register (>= passes + 3)
+
+
+def required_wait(wkind, rkind, reg_role):
+    """Wait states needed between a writer of kind ``wkind`` and a later instruction of
+    kind ``rkind`` touching the same register in role ``reg_role`` ('use', 'def', 'srcc')."""
+    if wkind == "mfma":
+        if rkind == "mfma":
+            return 0 if reg_role == "srcc" else MFMA_WAIT
+        return MFMA_WAIT
+    if rkind == "mfma":
+        if wkind in ("valu", "trans", "perm", "accw", "cmps"):
+            return 3
+        return 0
+    if wkind == "trans" and rkind in ("valu", "trans", "perm", "cmps", "accw", "vstore"):
+        return 2
+    if rkind == "perm" and wkind in ("valu", "trans", "cmps"):
+        return 2
+    if wkind == "perm" and rkind in ("valu", "trans", "cmps", "perm"):
+        return 2
+    if wkind == "cmps" and rkind in ("valu", "trans", "cmps"):
+        return 2
+    if wkind == "cmps" and rkind == "salu":
+        return 4
+    if wkind == "m0" and rkind == "dma":
+        return 1
+    if wkind == "accw" and rkind == "accr":
+        return 1
+    return 0
+
+
+class State:
+    def __init__(self):
+        self.last = {}      # reg -> (position, kind)
+        self.pos = 0        # wait states issued so far
+        self.lds = []       # outstanding LDS reads: list of sets of destination regs (issue order)
+
+    def copy(self):
+        s = State()
+        s.last = dict(self.last)
+        s.pos = self.pos
+        s.lds = [set(x) for x in self.lds]
+        return s
+
+
+def merge_states(a, b):
+    """Join of two control-flow paths: the most recent writer of every register, and the
+    LDS reads outstanding on either path (both paths must agree on LDS here)."""
+    s = State()
+    s.pos = max(a.pos, b.pos)
+    for st in (a, b):
+        for r, (p, k) in st.last.items():
+            p2 = p + (s.pos - st.pos)
+            if r not in s.last or p2 > s.last[r][0]:
+                s.last[r] = (p2, k)
+    s.lds = [set(x) for x in a.lds] if len(a.lds) >= len(b.lds) else [set(x) for x in b.lds]
+    return s
+
+
+def emit(ins, st, out):
+    """Append ``ins`` to ``out`` after the waits it needs; update the state."""
+    if ins.kind == "label":
+        out.append(ins.text)
+        return
+    touched = [(r, "use") for r in ins.uses] + [(r, "def") for r in ins.defs]
+    # LDS reads still in flight whose destination this instruction touches
+    if st.lds:
+        need = -1
+        for i, dset in enumerate(st.lds):
+            if any(r in dset for r, _ in touched):
+                need = i
+        if ins.kind in ("barrier",):
+            need = len(st.lds) - 1
+        if need >= 0:
+            left = len(st.lds) - need - 1
+            out.append("s_waitcnt lgkmcnt(%d)" % min(left, 15))
+            st.pos += 1
+            st.lds = st.lds[need + 1:]
+    wait = 0
+    for r, role in touched:
+        if r not in st.last:
+            continue
+        p, k = st.last[r]
+        rr = role
+        if ins.kind == "mfma" and ins.srcc and r in ins.srcc:
+            rr = "srcc"
+        need = required_wait(k, ins.kind, rr)
+        if need:
+            wait = max(wait, need - (st.pos - p))
+    while wait > 0:
+        n = min(wait, 16)
+        out.append("s_nop %d" % (n - 1))
+        st.pos += n
+        wait -= n
+    out.append(ins.text)
+    st.pos += 1
+    if ins.kind == "lds":
+        st.lds.append(set(ins.defs))
+        if len(st.lds) > 15:
+            raise RuntimeError("more than 15 LDS reads in flight")
+    for r in ins.defs:
+        st.last[r] = (st.pos - 1, ins.kind)
+
+
+def lower(items, st, out, uid):
+    """Lower a list of Ins / Skip / Loop / Cond into assembly lines."""
+    for it in items:
+        if isinstance(it, Ins):
+            emit(it, st, out)
+        elif isinstance(it, Skip):
+            out.append("s_cmp_eq_u64 %s, 0" % it.flag)
+            out.append("s_cbranch_scc1 %s_%s" % (it.label, uid))
+            st.pos += 2
+            before = st.copy()
+            lower(it.body, st, out, uid)
+            out.append("%s_%s:" % (it.label, uid))
+            st2 = merge_states(before, st)
+            st.last, st.pos, st.lds = st2.last, st2.pos, st2.lds
+        elif isinstance(it, Cond):
+            out.extend(it.test)
+            out.append("s_cbranch_scc0 %s_%s" % (it.label, uid))
+            st.pos += len(it.test) + 1
+            before = st.copy()
+            lower(it.body, st, out, uid)
+            out.append("%s_%s:" % (it.label, uid))
+            st2 = merge_states(before, st)
+            st.last, st.pos, st.lds = st2.last, st2.pos, st2.lds
+        elif isinstance(it, Loop):
+            # the state at the loop head joins the entry with the end of the body: run the
+            # body once to find its end state, then lower it for real from the join
+            if st.lds:
+                raise RuntimeError("LDS reads in flight at a loop head")
+            trial = st.copy()
+            lower(it.body, trial, [], uid)
+            head = merge_states(st, trial)
+            if head.lds:
+                raise RuntimeError("LDS reads in flight at the end of a loop body")
+            out.append("%s_%s:" % (it.label, uid))
+            st.last, st.pos, st.lds = head.last, head.pos, head.lds
+            lower(it.body, st, out, uid)
+            out.append("s_sub_u32 %s, %s, 1" % (it.counter, it.counter))
+            out.append("s_cmp_lg_u32 %s, 0" % it.counter)
+            out.append("s_cbranch_scc1 %s_%s" % (it.label, uid))
+            st.pos += 3
+        else:
+            raise TypeError(it)
+
+
+# ---------------------------------------------------------------- building blocks
+
+class Gen:
+    def __init__(self, elem, causal):
+        self.elem = elem            # "bf16" or "f16"
+        self.causal = causal
+        self.mfma_op = "v_mfma_f32_32x32x16_" + elem
+        self.cvt_op = "v_cvt_pk_bf16_f32" if elem == "bf16" else "v_cvt_pk_f16_f32"
+
+    # ---- operand reads from LDS
+    def k_read(self, i, kk, t):
+        """K operand for dims 16kk.. of keys 32t.. of the current K tile into staging i."""
+        return Ins("ds_read_b128 %s, %%[koff%d] offset:%d" % (vrange(KST(i), 4), kk, 8192 * t), "lds",
+                   defs=regs(KST(i), 4))
+
+    def v_reads(self, i, db, ks, t):
+        """V^T operand of dims 32db.. and keys 32t + 16ks.. (two transposing reads)."""
+        off = 8192 * t + 4096 * ks
+        return [Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i), 2), db, off), "lds",
+                    defs=regs(VST(i), 2)),
+                Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i) + 2, 2), 4 + db, off), "lds",
+                    defs=regs(VST(i) + 2, 2))]
+
+    def mfma_s(self, sbuf, rb, kk, st):
+        d = Sr(sbuf, rb)
+        src_c = "0" if kk == 0 else vrange(d, 16)
+        uses = regs(KST(st), 4) + regs(Qr(rb, kk), 4) + ([] if kk == 0 else regs(d, 16))
+        return Ins("%s %s, %s, %s, %s" % (self.mfma_op, vrange(d, 16), vrange(KST(st), 4), vrange(Qr(rb, kk), 4),
+                                          src_c), "mfma", defs=regs(d, 16), uses=uses,
+                   srcc=set(regs(d, 16)) if kk else None)
+
+    def mfma_pv(self, pbuf, rb, db, ks, st):
+        o = Or(rb, db)
+        uses = regs(VST(st), 4) + regs(Pr(pbuf, rb, ks), 4) + regs(o, 16, "a")
+        return Ins("%s a[%d:%d], %s, %s, a[%d:%d]" % (self.mfma_op, o, o + 15, vrange(VST(st), 4),
+                                                      vrange(Pr(pbuf, rb, ks), 4), o, o + 15),
+                   "mfma", defs=regs(o, 16, "a"), uses=uses, srcc=set(regs(o, 16, "a")))
+
+    # ---- the product streams of one half: list of (reads, mfma) with staging slots
+    def s_stream(self, sbuf, t, rbs):
+        """S(h+1) into S buffer sbuf from K tile rows 32t..: per kk one K read feeding the
+        products of every active row block."""
+        out = []
+        for kk in range(8):
+            st = kk % 4
+            prods = [self.mfma_s(sbuf, rb, kk, st) for rb in rbs]
+            out.append(([self.k_read(st, kk, t)], prods))
+        return out
+
+    def pv_stream(self, pbuf, t, rbs):
+        out = []
+        n = 0
+        for ks in range(2):
+            for db in range(4):
+                st = n % 4
+                n += 1
+                prods = [self.mfma_pv(pbuf, rb, db, ks, st) for rb in rbs]
+                out.append((self.v_reads(st, db, ks, t), prods))
+        return out
+
+
+def t(n):
+    if n >= NTMP - 1:
+        raise ValueError("temporary register index")
+    return TMP0 + n
+
+
+def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
+    """The vector work of one half.
+
+    masks: dict rb -> None | "tri" | "lim"  (lim: keys past the valid count, threshold in
+    %[dlim]); dead: row blocks whose keys are all masked in this half (P = 0, alpha = 1).
+    first: the reference may still be -inf (first half, or a masked half of the first tile):
+    use 0 as the exp reference while it is.
+    """
+    live = [rb for rb in (0, 1) if rb not in dead]
+    streams = {rb: [] for rb in live}
+    ops_dead = []
+    for rb in dead:
+        for ks in range(2):
+            for j in range(4):
+                ops_dead.append(Ins("v_mov_b32 %s, 0" % vr(Pr(pbuf, rb, ks) + j), "valu", defs=[vr(Pr(pbuf, rb, ks) + j)]))
+        ops_dead.append(Ins("v_mov_b32 %s, 1.0" % vr(ALr(par, rb)), "valu", defs=[vr(ALr(par, rb))]))
+    mask_sgprs = {0: ["vcc", "%[mk1]", "%[mk2]", "%[mk3]"], 1: ["%[mk4]", "%[mk5]", "%[mk6]", "%[mk7]"]}
+    for idx, rb in enumerate(live):
+        mask_sgpr = mask_sgprs[rb]
+        o = streams[rb]
+        s = Sr(sbuf, rb)
+        base = 12 * idx      # temporaries of this row block: t(base) .. t(base + 11)
+        T = lambda n: vr(t(base + n))
+        m = masks.get(rb)
+        if m:
+            thr = "%[dmask]" if m == "tri" else "%[dlim]"
+            # key index within the half of register r of this lane, minus 4*hi: 8*(r>>2) + (r&3)
+            seq = []
+            for r in range(16):
+                kc = 8 * (r >> 2) + (r & 3)
+                mk = mask_sgpr[r % 4]
+                if mk == "vcc":
+                    cmp_ = Ins("v_cmp_le_i32_e32 vcc, %d, %s" % (kc, thr), "cmps", defs=["vcc"])
+                    sel = Ins("v_cndmask_b32_e32 %s, %s, %s, vcc" % (vr(s + r), vr(NEGINF), vr(s + r)), "valu",
+                              defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), "vcc"])
+                else:
+                    cmp_ = Ins("v_cmp_le_i32_e64 %s, %d, %s" % (mk, kc, thr), "cmps", defs=[mk])
+                    sel = Ins("v_cndmask_b32_e64 %s, %s, %s, %s" % (vr(s + r), vr(NEGINF), vr(s + r), mk), "valu",
+                              defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), mk])
+                seq.append((cmp_, sel))
+            for r in range(16):
+                o.append(seq[r][0])
+                if r >= 3:
+                    o.append(seq[r - 3][1])
+            for r in range(13, 16):
+                o.append(seq[r][1])
+        # row max over this lane's 16 scores
+        S = lambda r: vr(s + r)
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(0), S(0), S(1), S(2)), "valu", defs=[T(0)], uses=[S(0), S(1), S(2)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(1), S(3), S(4), S(5)), "valu", defs=[T(1)], uses=[S(3), S(4), S(5)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(2), S(6), S(7), S(8)), "valu", defs=[T(2)], uses=[S(6), S(7), S(8)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(3), S(9), S(10), S(11)), "valu", defs=[T(3)], uses=[S(9), S(10), S(11)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(4), S(12), S(13), S(14)), "valu", defs=[T(4)], uses=[S(12), S(13), S(14)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(0), T(0), T(1), T(2)), "valu", defs=[T(0)], uses=[T(0), T(1), T(2)]))
+        o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(3), T(3), T(4), S(15)), "valu", defs=[T(3)], uses=[T(3), T(4), S(15)]))
+        o.append(Ins("v_max_f32_e32 %s, %s, %s" % (T(0), T(0), T(3)), "valu", defs=[T(0)], uses=[T(0), T(3)]))
+        # the other lane half holds the same row: exchange and take the larger
+        o.append(Ins("v_mov_b32_e32 %s, %s" % (T(1), T(0)), "valu", defs=[T(1)], uses=[T(0)]))
+        o.append(Ins("v_permlane32_swap_b32_e32 %s, %s" % (T(0), T(1)), "perm", defs=[T(0), T(1)], uses=[T(0), T(1)]))
+        o.append(Ins("v_max_f32_e32 %s, %s, %s" % (T(0), T(0), T(1)), "valu", defs=[T(0)], uses=[T(0), T(1)]))
+        # scaled max, lazy move of the reference (only past 2^8 of growth)
+        o.append(Ins("v_mul_f32_e32 %s, %%[c], %s" % (T(0), T(0)), "valu", defs=[T(0)], uses=[T(0)]))
+        o.append(Ins("v_add_f32_e32 %s, 0x41000000, %s" % (T(2), vr(Mr(rb))), "valu", defs=[T(2)], uses=[vr(Mr(rb))]))
+        gb = "%%[g%d%d]" % (par, rb)
+        o.append(Ins("v_cmp_gt_f32_e64 %s, %s, %s" % (gb, T(0), T(2)), "cmps", defs=[gb], uses=[T(0), T(2)]))
+        o.append(Ins("v_cndmask_b32_e64 %s, %s, %s, %s" % (T(3), vr(Mr(rb)), T(0), gb), "valu", defs=[T(3)],
+                     uses=[vr(Mr(rb)), T(0), gb]))
+        if first:
+            # nothing finite yet on this row: 0 as the exp reference (P = 0, alpha = 0)
+            gk = mask_sgpr[1]
+            o.append(Ins("v_cmp_eq_f32_e64 %s, %s, %s" % (gk, vr(NEGINF), T(3)), "cmps", defs=[gk],
+                         uses=[vr(NEGINF), T(3)]))
+            o.append(Ins("v_cndmask_b32_e64 %s, %s, 0, %s" % (T(4), T(3), gk), "valu", defs=[T(4)],
+                         uses=[T(3), gk]))
+            ref = T(4)
+        else:
+            ref = T(3)
+        o.append(Ins("v_sub_f32_e32 %s, %s, %s" % (T(2), vr(Mr(rb)), ref), "valu", defs=[T(2)], uses=[vr(Mr(rb)), ref]))
+        o.append(Ins("v_exp_f32_e32 %s, %s" % (vr(ALr(par, rb)), T(2)), "trans", defs=[vr(ALr(par, rb))], uses=[T(2)]))
+        o.append(Ins("v_mov_b32_e32 %s, %s" % (vr(Mr(rb)), T(3)), "valu", defs=[vr(Mr(rb))], uses=[T(3)]))
+        # P = exp2(S c - m), in place; row sums in four chains; P rounded for the PV product
+        pe = []
+        for r in range(16):
+            pe.append(Ins("v_fma_f32 %s, %s, %%[c], -%s" % (S(r), S(r), ref), "valu", defs=[S(r)], uses=[S(r), ref]))
+            pe.append(Ins("v_exp_f32_e32 %s, %s" % (S(r), S(r)), "trans", defs=[S(r)], uses=[S(r)]))
+        o.extend(pe)
+        sums = []
+        for c in range(4):
+            sums.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + c), S(2 * c), S(2 * c + 1)), "valu",
+                            defs=[T(5 + c)], uses=[S(2 * c), S(2 * c + 1)]))
+        for r in range(8, 16):
+            c = r % 4
+            sums.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + c), S(r), T(5 + c)), "valu", defs=[T(5 + c)],
+                            uses=[S(r), T(5 + c)]))
+        cvts = []
+        for ks in range(2):
+            for j in range(4):
+                p = Pr(pbuf, rb, ks) + j
+                cvts.append(Ins("%s %s, %s, %s" % (g.cvt_op, vr(p), S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)), "valu",
+                                defs=[vr(p)], uses=[S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)]))
+        # interleave sums and conversions
+        for a, b in zip(sums[:8], cvts):
+            o.append(a)
+            o.append(b)
+        o.extend(sums[8:])
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5), T(5), T(6)), "valu", defs=[T(5)], uses=[T(5), T(6)]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(7), T(7), T(8)), "valu", defs=[T(7)], uses=[T(7), T(8)]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5), T(5), T(7)), "valu", defs=[T(5)], uses=[T(5), T(7)]))
+        o.append(Ins("v_fma_f32 %s, %s, %s, %s" % (vr(Lr(rb)), vr(Lr(rb)), vr(ALr(par, rb)), T(5)), "valu",
+                     defs=[vr(Lr(rb))], uses=[vr(Lr(rb)), vr(ALr(par, rb)), T(5)]))
+    # interleave the row blocks' streams
+    out = list(ops_dead)
+    ls = [streams[rb] for rb in live]
+    i = 0
+    while any(i < len(x) for x in ls):
+        for x in ls:
+            if i < len(x):
+                out.append(x[i])
+        i += 1
+    # the wave's "any row moved its reference" ballot for this parity
+    gs = ["%%[g%d%d]" % (par, rb) for rb in live]
+    if len(gs) == 2:
+        out.append(Ins("s_or_b64 %%[ga%d], %s, %s" % (par, gs[0], gs[1]), "salu", defs=["%%[ga%d]" % par], uses=gs))
+    else:
+        out.append(Ins("s_mov_b64 %%[ga%d], %s" % (par, gs[0]), "salu", defs=["%%[ga%d]" % par], uses=gs))
+    return out
+
+
+def rescale_block(par, rbs):
+    """O *= alpha[par] on the row blocks rbs: read, multiply, write back, 8 at a time."""
+    out = [Ins("s_nop 7", "nop")]
+    regs_list = [(rb, Or(rb, db) + r) for rb in rbs for db in range(4) for r in range(16)]
+    for i in range(0, len(regs_list), 8):
+        chunk = regs_list[i:i + 8]
+        for j, (rb, a) in enumerate(chunk):
+            out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (vr(t(j)), a), "accr", defs=[vr(t(j))], uses=["a%d" % a]))
+        for j, (rb, a) in enumerate(chunk):
+            out.append(Ins("v_mul_f32_e32 %s, %s, %s" % (vr(t(j)), vr(ALr(par, rb)), vr(t(j))), "valu",
+                           defs=[vr(t(j))], uses=[vr(t(j)), vr(ALr(par, rb))]))
+        for j, (rb, a) in enumerate(chunk):
+            out.append(Ins("v_accvgpr_write_b32 a%d, %s" % (a, vr(t(j))), "accw", defs=["a%d" % a], uses=[vr(t(j))]))
+    return out
+
+
+def merge_half(prod_streams, valu, extra, lead=2):
+    """Interleave one half: the product streams (list of (reads, products) in order), the
+    vector work and the extra instructions (DMA, toggles).  Each group's reads are issued
+    ``lead`` groups ahead of its products; the vector and extra work is spread evenly over
+    the products."""
+    groups = []
+    for stream in prod_streams:
+        groups.extend(stream)
+    nprod = sum(len(p) for _, p in groups)
+    out = []
+    # initial reads
+    for k in range(min(lead, len(groups))):
+        out.extend(groups[k][0])
+    vi = 0
+    ei = 0
+    done = 0
+    for gi, (_, prods) in enumerate(groups):
+        if gi + lead < len(groups):
+            out.extend(groups[gi + lead][0])
+        for p in prods:
+            out.append(p)
+            done += 1
+            vt = (len(valu) * done + nprod - 1) // nprod if nprod else len(valu)
+            et = (len(extra) * done + nprod - 1) // nprod if nprod else len(extra)
+            while ei < et:
+                out.append(extra[ei])
+                ei += 1
+            while vi < vt:
+                out.append(valu[vi])
+                vi += 1
+    out.extend(extra[ei:])
+    out.extend(valu[vi:])
+    return out
+
+
+# ---------------------------------------------------------------- tile loads (LDS DMA)
+
+def dma_tile(which):
+    """This wave's half of one 64-key K or V tile: 8 slices of 1 KiB, slice ii = wave + 2i,
+    from %[<which>src] (byte offset of the tile in the head) into the buffer at
+    %[<which>dst] (LDS address of this wave's first slice in the tile's buffer)."""
+    out = []
+    rs = "%[krs]" if which == "k" else "%[vrs]"
+    for i in range(8):
+        out.append(Ins("s_add_u32 m0, %%[%sdst], %d" % (which, 2048 * i), "m0", defs=["m0"]))
+        out.append(Ins("s_add_u32 %%[soff], %%[%ssrc], %d" % (which, 2048 * i), "salu", defs=["%[soff]"]))
+        out.append(Ins("buffer_load_dwordx4 %%[dma%d], %s, %%[soff] offen lds" % (i & 1, rs), "dma",
+                       uses=["m0", "%[soff]"]))
+    return out
+
+
+def advance_k():
+    """Next K tile: source +16 KiB, LDS buffer toggled."""
+    return [Ins("s_add_u32 %[ksrc], %[ksrc], 16384", "salu", defs=["%[ksrc]"], uses=["%[ksrc]"]),
+            Ins("s_xor_b32 %[kdst], %[kdst], 16384", "salu", defs=["%[kdst]"], uses=["%[kdst]"])]
+
+
+def advance_v():
+    return [Ins("s_add_u32 %[vsrc], %[vsrc], 16384", "salu", defs=["%[vsrc]"], uses=["%[vsrc]"]),
+            Ins("s_xor_b32 %[vdst], %[vdst], 16384", "salu", defs=["%[vdst]"], uses=["%[vdst]"])]
+
+
+def toggle_reads():
+    """Switch the K and V operand reads to the other buffer of each."""
+    out = []
+    for kk in range(8):
+        out.append(Ins("v_xor_b32_e32 %%[koff%d], 0x4000, %%[koff%d]" % (kk, kk), "valu",
+                       defs=["%%[koff%d]" % kk], uses=["%%[koff%d]" % kk]))
+    for i in range(8):
+        out.append(Ins("v_xor_b32_e32 %%[voff%d], 0x4000, %%[voff%d]" % (i, i), "valu",
+                       defs=["%%[voff%d]" % i], uses=["%%[voff%d]" % i]))
+    return out
+
+
+def barrier():
+    return [Ins("s_waitcnt vmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
+
+
+# ---------------------------------------------------------------- the program
+
+def half_interleaved(g, s_next, pv_prev, soft, rescale_par, extra=()):
+    """One half with the S and PV products alternating (used when no rescale can intervene
+    between them: the rescale for the previous half is applied before this half starts)."""
+    ps = []
+    s_groups = g.s_stream(*s_next) if s_next else []
+    pv_groups = g.pv_stream(*pv_prev) if pv_prev else []
+    merged = []
+    for i in range(max(len(s_groups), len(pv_groups))):
+        if i < len(s_groups):
+            merged.append(s_groups[i])
+        if i < len(pv_groups):
+            merged.append(pv_groups[i])
+    out = []
+    if pv_groups and rescale_par is not None:
+        out.append(Skip("%%[ga%d]" % rescale_par, rescale_block(rescale_par, pv_prev[2]), "L_rs%d" % len(g.labels)))
+        g.labels.append(1)
+    out.extend(merge_half([merged], list(soft), list(extra)))
+    return out
+
+
+def build(elem, causal):
+    g = Gen(elem, causal)
+    g.labels = []
+    all_rb = (0, 1)
+    prog = []
+    # ---- setup: O = 0, m = -inf, l = 0, Q loads (sign folded), -inf constant
+    prog.append(Ins("v_mov_b32 %s, %s" % (vr(NEGINF), NEG_INF_BITS), "valu", defs=[vr(NEGINF)]))
+    for rb in all_rb:
+        prog.append(Ins("v_mov_b32 %s, %s" % (vr(Mr(rb)), NEG_INF_BITS), "valu", defs=[vr(Mr(rb))]))
+        prog.append(Ins("v_mov_b32 %s, 0" % vr(Lr(rb)), "valu", defs=[vr(Lr(rb))]))
+    prog.append(Ins("s_mov_b32 %[kit], 1", "salu", defs=["%[kit]"]))
+    prog.append(Ins("v_add_u32_e32 %s, 0x2000, %%[qoff]" % vr(t(0)), "valu", defs=[vr(t(0))]))
+    for rb in all_rb:
+        for kk in range(8):
+            base = "%[qoff]" if rb == 0 else vr(t(0))
+            prog.append(Ins("buffer_load_dwordx4 %s, %s, %%[qrs], 0 offen offset:%d" % (vrange(Qr(rb, kk), 4), base, 32 * kk),
+                            "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else [vr(t(0))]))
+    for a in range(128):
+        prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
+    prog.append(Ins("s_waitcnt vmcnt(0)", "wait"))
+    for r in range(64):
+        prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
+    # ---- first tiles: K(0), K(1) (if any), V(0)
+    prog.extend(dma_tile("k"))
+    prog.extend(advance_k())
+    prog.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k"), "L_k1"))
+    prog.extend(advance_k())
+    prog.extend(dma_tile("v"))
+    prog.extend(advance_v())
+    prog.extend(barrier())
+    # S(0) alone
+    prog.extend(merge_half([g.s_stream(0, 0, all_rb)], [], []))
+
+    tri = "tri" if causal else "lim"
+    maskA = {0: "tri"} if causal else {0: "lim", 1: "lim"}
+    maskB = {1: "tri"} if causal else {0: "lim", 1: "lim"}
+    deadB = (0,) if causal else ()
+    rbB = (1,) if causal else all_rb
+    lim_ops = lambda which: [] if causal else [
+        Ins("v_sub_u32_e32 %%[dlim], %%[%s], %%[hi4]" % which, "valu", defs=["%[dlim]"])]
+
+    # iteration k: barrier B_k, loads K(k+1) and V(k), halves 2k-1 and 2k
+    def iter_head(cond_k, cond_v):
+        out = toggle_reads()
+        out.extend(barrier())
+        ek = dma_tile("k") + advance_k()
+        ev = dma_tile("v") + advance_v()
+        if cond_k:
+            ek = [Cond(["s_add_u32 %[soff], %[kit], 1", "s_cmp_lt_u32 %[soff], %[nt]"], ek, "L_ck%d" % len(g.labels))]
+            g.labels.append(1)
+        if cond_v:
+            ev = [Cond(["s_cmp_lt_u32 %[kit], %[nt]"], ev, "L_cv%d" % len(g.labels))]
+            g.labels.append(1)
+        return out, ek + ev
+
+    # ---- L >= 1 path: half 0 unmasked
+    pathA = []
+    pathA.extend(half_interleaved(g, (1, 1, all_rb), None,
+                                  softmax_ops(g, 0, 0, 0, {}, True, ()), None))
+    pathA.append(Ins("s_mov_b64 %[ga0], 0", "salu", defs=["%[ga0]"]))      # O is zero: no rescale
+    # steady loop over k = 1 .. L-1
+    head, dmas = iter_head(False, False)
+    body = list(head)
+    body.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
+                                 softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas))
+    body.extend(half_interleaved(g, (1, 1, all_rb), (1, 1, all_rb),
+                                 softmax_ops(g, 0, 0, 0, {}, False, ()), 1, []))
+    body.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+    pathA.append(Ins("s_sub_u32 %[cnt], %[last], 1", "salu", defs=["%[cnt]"]))
+    pathA.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", body, "L_loop")], "L_skiploop"))
+    # iteration L: half 2L-1 unmasked, half 2L masked A
+    head, dmas = iter_head(True, False)
+    pathA.extend(head)
+    pathA.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
+                                  softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas))
+    pathA.extend(lim_ops("limA"))
+    pathA.extend(half_interleaved(g, (1, 1, rbB), (1, 1, all_rb),
+                                  softmax_ops(g, 0, 0, 0, maskA, False, ()), 1, []))
+    pathA.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+    pathA.append(Ins("s_branch L_tailB_%=", "branch"))
+    # ---- L == 0 path: half 0 masked A
+    pathB = []
+    pathB.extend(lim_ops("limA"))
+    pathB.extend(half_interleaved(g, (1, 1, rbB), None,
+                                  softmax_ops(g, 0, 0, 0, maskA, True, ()), None))
+    pathB.append(Ins("s_mov_b64 %[ga0], 0", "salu", defs=["%[ga0]"]))
+    # ---- tail B (iteration L+1): half 2L+1 (PV(2L), softmax masked B), half 2L+2 (PV(2L+1))
+    tail = []
+    head, dmas = iter_head(True, True)
+    tail.extend(head)
+    tail.extend(lim_ops("limB"))
+    tail.extend(half_interleaved(g, None, (0, 0, all_rb),
+                                 softmax_ops(g, 1, 1, 1, maskB, False, deadB), 0, dmas))
+    tail.extend(half_interleaved(g, None, (1, 1, rbB), [], 1, []))
+    tail.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+    # the wave is done with its rows: store O and LSE
+    tail.extend(epilogue(g))
+    # the waves still walking tiles need this wave's share of the loads and its barriers
+    duty = []
+    head, dmas = iter_head(True, True)
+    duty.extend(head)
+    duty.extend(dmas)
+    duty.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+    tail.append(Ins("s_sub_u32 %[cnt], %[nt], %[last]", "salu", defs=["%[cnt]"]))
+    tail.append(Ins("s_sub_u32 %[cnt], %[cnt], 1", "salu", defs=["%[cnt]"]))
+    tail.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", duty, "L_duty")], "L_skipduty"))
+    tail.append(Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"))
+    return g, prog, pathA, pathB, tail
+
+
+def epilogue(g):
+    out = [Ins("s_nop 15", "nop"), Ins("s_nop 15", "nop")]
+    for rb in (0, 1):
+        L = vr(Lr(rb))
+        tl = vr(t(20))
+        out.append(Ins("v_mov_b32_e32 %s, %s" % (tl, L), "valu", defs=[tl], uses=[L]))
+        out.append(Ins("v_permlane32_swap_b32_e32 %s, %s" % (L, tl), "perm", defs=[L, tl], uses=[L, tl]))
+        out.append(Ins("v_add_f32_e32 %s, %s, %s" % (L, L, tl), "valu", defs=[L], uses=[L, tl]))
+        inv = vr(t(21))
+        out.append(Ins("v_rcp_f32_e32 %s, %s" % (inv, L), "trans", defs=[inv], uses=[L]))
+        lg = vr(t(22))
+        out.append(Ins("v_log_f32_e32 %s, %s" % (lg, L), "trans", defs=[lg], uses=[L]))
+        out.append(Ins("v_add_f32_e32 %s, %s, %s" % (lg, vr(Mr(rb)), lg), "valu", defs=[lg], uses=[lg, vr(Mr(rb))]))
+        out.append(Ins("v_mul_f32_e32 %s, 0x3f317218, %s" % (lg, lg), "valu", defs=[lg], uses=[lg]))   # ln 2
+        loff = "%[loff]" if rb == 0 else vr(t(19))
+        if rb == 1:
+            out.append(Ins("v_add_u32_e32 %s, 0x80, %%[loff]" % vr(t(19)), "valu", defs=[vr(t(19))]))
+        out.append(Ins("buffer_store_dword %s, %s, %%[lrs], 0 offen" % (lg, loff), "vstore", uses=[lg, loff]))
+        ooff = "%[ooff]" if rb == 0 else vr(t(18))
+        if rb == 1:
+            out.append(Ins("v_add_u32_e32 %s, 0x2000, %%[ooff]" % vr(t(18)), "valu", defs=[vr(t(18))]))
+        for db in range(4):
+            for gq in range(4):
+                a0 = Or(rb, db) + 4 * gq
+                tv = [vr(t(j)) for j in range(4)]
+                for j in range(4):
+                    out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (tv[j], a0 + j), "accr", defs=[tv[j]], uses=["a%d" % (a0 + j)]))
+                for j in range(4):
+                    out.append(Ins("v_mul_f32_e32 %s, %s, %s" % (tv[j], inv, tv[j]), "valu", defs=[tv[j]], uses=[tv[j], inv]))
+                pk = vr(t(8 + 2 * gq))
+                pk2 = vr(t(9 + 2 * gq))
+                out.append(Ins("%s %s, %s, %s" % (g.cvt_op, pk, tv[0], tv[1]), "valu", defs=[pk], uses=tv[:2]))
+                out.append(Ins("%s %s, %s, %s" % (g.cvt_op, pk2, tv[2], tv[3]), "valu", defs=[pk2], uses=tv[2:]))
+                off = (32 * db + 8 * gq) * 2
+                out.append(Ins("buffer_store_dwordx2 %s, %s, %%[ors], 0 offen offset:%d" % (
+                    "v[%d:%d]" % (t(8 + 2 * gq), t(9 + 2 * gq)), ooff, off), "vstore",
+                    uses=[pk, pk2, ooff]))
+    return out
+
+
+def assemble(elem, causal):
+    g, prog, pathA, pathB, tail = build(elem, causal)
+    st = State()
+    out = []
+    lower(prog, st, out, "%=")
+    out.append("s_cmp_eq_u32 %[last], 0")
+    out.append("s_cbranch_scc1 L_pathB_%=")
+    st.pos += 2
+    stB = st.copy()
+    lower(pathA, st, out, "%=")
+    out.append("L_pathB_%=:")
+    lower(pathB, stB, out, "%=")
+    out.append("L_tailB_%=:")
+    st2 = merge_states(st, stB)
+    lower(tail, st2, out, "%=")
+    return out
+
+
+def c_string(lines):
+    return "\n".join('    "%s\\n"' % l.replace('"', '\\"') for l in lines)
+
+
+def main():
+    parts = ["// Generated by gen_fwd_kloop.py; do not edit.  The key loop of the 64-rows-per-wave\n"
+             "// forward (fa_fwd_w64.hip) as gfx950 assembly, one string per element type and mask.\n"
+             "#pragma once\n"]
+    for elem in ("bf16", "f16"):
+        for causal in (False, True):
+            lines = assemble(elem, causal)
+            name = "FA_KLOOP_%s_%s" % (elem.upper(), "CAUSAL" if causal else "FULL")
+            parts.append("#define %s \\\n%s\n" % (name, " \\\n".join('    "%s\\n"' % l for l in lines)))
+    text = "\n".join(parts)
+    with open(OUT, "w") as f:
+        f.write(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
