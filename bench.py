@@ -54,6 +54,8 @@ PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = {
     "bf16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_mfma16.hip",
     "f16": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_mfma16.hip",
+    # the d = 128 forward of 16-bit inputs: 64 rows per wave, its key loop generated as assembly
+    "w64": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_w64.hip",
     "f32": "flashattention_online_softmax_fwd_amd/csrc/fa_fwd_f32.hip",
     "merge": "flashattention_online_softmax_fwd_amd/csrc/fa_merge.hip",
     "softmax": "flashattention_online_softmax_fwd_amd/csrc/fa_softmax.hip",
@@ -70,8 +72,26 @@ def kernel_hash(source: str) -> str:
     path = KERNEL_SOURCES[source]
     with open(os.path.join(ROOT, path), "rb") as f:
         data = f.read()
+    if source == "w64":   # the generated key loop is part of the kernel
+        with open(os.path.join(ROOT, os.path.dirname(path), "fa_fwd_kloop.inc"), "rb") as f:
+            data += f.read()
     flags = " ".join(build.device_flags(os.path.basename(path))).encode()
     return hashlib.sha256(data + b"\0" + flags).hexdigest()
+
+
+def forward_kernel(w):
+    """(KERNEL_SOURCES key, kernel name) of the forward the library dispatches for ``w`` by
+    default: fp32 has its own kernel; 16-bit inputs at d = 128 run the 64-rows-per-wave
+    kernel, in 256-row workgroups (4 waves) when the grid holds at least 512 of them and in
+    128-row workgroups (2 waves) otherwise; 16-bit inputs at d = 64 run fwd16_kernel."""
+    if w.dtype == "f32":
+        return "f32", "fa::fwd_f32_kernel"
+    if w.d == 128:
+        units = w.B * w.Hq
+        nw = 4 if units * ((w.N + 255) // 256) >= 512 else 2
+        return "w64", "fa::fwd_w64_kernel<%s, %s, %d>" % (
+            "__bf16" if w.dtype == "bf16" else "_Float16", "true" if w.causal else "false", nw)
+    return w.dtype, "fa::fwd16_kernel<%s>" % w.dtype
 
 
 def traffic_for(workload: str, source: str):
@@ -270,6 +290,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget, precondition_s=0.0):
     avg_launch_ms = sum(per_ms) / len(per_ms)
     achieved = w.flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    src, kname = forward_kernel(w)
     rec = {
         "metric": metric_for(w),
         "value": tflops,
@@ -298,8 +319,8 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget, precondition_s=0.0):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": traffic_for(w.name, w.dtype),
-            "kernel": "fa::fwd_f32_kernel" if w.dtype == "f32" else "fa::fwd16_kernel<%s>" % w.dtype,
+            "traffic": traffic_for(w.name, src),
+            "kernel": kname,
             "avg_launch_ms": avg_launch_ms,
             "min_launch_ms": min(per_ms),
             "median_launch_ms": sorted(per_ms)[len(per_ms) // 2],
@@ -310,7 +331,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget, precondition_s=0.0):
         },
         "preconditioning": pre,
         "clock": clock,
-        "counters": counters_for(w.name, w.dtype),
+        "counters": counters_for(w.name, src),
     }
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, o, lse, cpu_budget)

@@ -62,15 +62,19 @@ namespace fa {
     "a76", "a77", "a78", "a79", "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", \
     "a91", "a92", "a93", "a94", "a95", "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104",   \
     "a105", "a106", "a107", "a108", "a109", "a110", "a111", "a112", "a113", "a114", "a115", "a116", "a117",  \
-    "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "vcc", "m0", "scc",       \
-    "memory"
+    "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "a128", "a129", "a130",  \
+    "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143",  \
+    "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156",  \
+    "a157", "a158", "a159", "vcc", "m0", "scc", "memory"
 
-template <typename E, bool CAUSAL>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename E, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_w64_kernel(const FwdParams p)
 {
+    static_assert(NW == 2 || NW == 4, "two or four waves of 64 rows");
     constexpr int D = 128;
     constexpr int ROWB = D * 2;
+    constexpr int BM = 64 * NW;   // query rows of the workgroup
     // K0, K1, V0, V1.  Aligned to 32 KiB: the walk switches buffers by flipping bit 14 of
     // the addresses.
     __shared__ __attribute__((aligned(32768))) char lds[65536];
@@ -113,7 +117,7 @@ fwd_w64_kernel(const FwdParams p)
         cyc0 = __builtin_amdgcn_s_memtime();
     }
 
-    const int q0 = qt * 128;
+    const int q0 = qt * BM;
     const int row0 = q0 + 64 * wave;                    // the wave's first query row
     const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
     const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
@@ -141,20 +145,21 @@ fwd_w64_kernel(const FwdParams p)
             voff[4 * r + dt] = (int)ldsb + 49152 + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
         }
     }
-    // Tile loads: slice ii = wave + 2i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
+    // Tile loads: slice ii = wave + NW i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
     // lane's 16 bytes are row 4ii + lane/16, physical chunk lane%16, i.e. logical chunk
-    // (lane%16) ^ swz(row).  Only ii's low two bits enter the swizzle: two patterns (i even, odd).
+    // (lane%16) ^ swz(row).  Only ii's low two bits enter the swizzle: two patterns (i even, odd;
+    // the same pattern when NW = 4).
     int dma[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int row = 4 * (wave + 2 * e) + (lane >> 4);
+        const int row = 4 * (wave + NW * e) + (lane >> 4);
         dma[e] = 1024 * wave + (lane >> 4) * ROWB + 16 * ((lane & 15) ^ swz<D>(row));
     }
     const int dmask = l32 - 4 * hi;   // causal: key 8(r>>2) + (r&3) + 4hi of a diagonal half visible iff <= row l32
     const int hi4 = 4 * hi;
 
     // Key tiles of 64 for the workgroup; the last one this wave's rows need.
-    const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
+    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int nt = (kv_end + 63) / 64;
     const int last = CAUSAL ? min(nt - 1, q0 / 64 + wave) : nt - 1;
     const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
@@ -184,12 +189,22 @@ fwd_w64_kernel(const FwdParams p)
                    [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
                    [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip)                                                 \
                  : FA_W64_CLOBBERS)
-    if constexpr (__is_same(E, __bf16)) {
-        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL);
-        else FA_W64_ASM(FA_KLOOP_BF16_FULL);
+    if constexpr (NW == 2) {
+        if constexpr (__is_same(E, __bf16)) {
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W2);
+            else FA_W64_ASM(FA_KLOOP_BF16_FULL_W2);
+        } else {
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W2);
+            else FA_W64_ASM(FA_KLOOP_F16_FULL_W2);
+        }
     } else {
-        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL);
-        else FA_W64_ASM(FA_KLOOP_F16_FULL);
+        if constexpr (__is_same(E, __bf16)) {
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W4);
+            else FA_W64_ASM(FA_KLOOP_BF16_FULL_W4);
+        } else {
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W4);
+            else FA_W64_ASM(FA_KLOOP_F16_FULL_W4);
+        }
     }
 #undef FA_W64_ASM
 
@@ -197,35 +212,45 @@ fwd_w64_kernel(const FwdParams p)
         const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
         const unsigned long long real1 = __builtin_amdgcn_s_memrealtime();
         typedef __attribute__((ext_vector_type(4))) unsigned long long u64x4;
-        *(u64x4*)(p.stamps + ((size_t)bid * 2 + wave) * 4) = u64x4{real0, real1, cyc0, cyc1};
+        *(u64x4*)(p.stamps + ((size_t)bid * NW + wave) * 4) = u64x4{real0, real1, cyc0, cyc1};
     }
 }
 
-template __global__ void fwd_w64_kernel<__bf16, false>(const FwdParams);
-template __global__ void fwd_w64_kernel<__bf16, true>(const FwdParams);
-template __global__ void fwd_w64_kernel<_Float16, false>(const FwdParams);
-template __global__ void fwd_w64_kernel<_Float16, true>(const FwdParams);
+#define FA_W64_INSTANTIATE(NW)                                                  \
+    template __global__ void fwd_w64_kernel<__bf16, false, NW>(const FwdParams);   \
+    template __global__ void fwd_w64_kernel<__bf16, true, NW>(const FwdParams);    \
+    template __global__ void fwd_w64_kernel<_Float16, false, NW>(const FwdParams); \
+    template __global__ void fwd_w64_kernel<_Float16, true, NW>(const FwdParams);
+FA_W64_INSTANTIATE(2)
+FA_W64_INSTANTIATE(4)
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 namespace {
 
-template <typename E, bool CAUSAL>
+template <typename E, bool CAUSAL, int NW>
 hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
 {
     const long long units = (long long)p.B * p.Hq;
     FwdParams args = p;
     args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL>, dim3((unsigned)(units * p.n_qtiles)), dim3(128),
-                           kargs, 0, stream);
+    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL, NW>, dim3((unsigned)(units * p.n_qtiles)),
+                           dim3(64 * NW), kargs, 0, stream);
 }
 
 }  // namespace
 
-const KernelEntry kBf16W64Kernels[] = {{1, 128, 128, 64, 0, &launch_w64<__bf16, false>, 2},
-                                       {1, 128, 128, 64, 1, &launch_w64<__bf16, true>, 2}};
-const KernelEntry kF16W64Kernels[] = {{2, 128, 128, 64, 0, &launch_w64<_Float16, false>, 2},
-                                      {2, 128, 128, 64, 1, &launch_w64<_Float16, true>, 2}};
+// 256-row workgroups first: one K/V tile load per CU instead of two (2-3% faster on the causal
+// d = 128 workloads); the host falls back to 128-row workgroups for grids too small to give
+// every CU two of them.
+const KernelEntry kBf16W64Kernels[] = {{1, 128, 256, 64, 0, &launch_w64<__bf16, false, 4>, 4},
+                                       {1, 128, 256, 64, 1, &launch_w64<__bf16, true, 4>, 4},
+                                       {1, 128, 128, 64, 0, &launch_w64<__bf16, false, 2>, 2},
+                                       {1, 128, 128, 64, 1, &launch_w64<__bf16, true, 2>, 2}};
+const KernelEntry kF16W64Kernels[] = {{2, 128, 256, 64, 0, &launch_w64<_Float16, false, 4>, 4},
+                                      {2, 128, 256, 64, 1, &launch_w64<_Float16, true, 4>, 4},
+                                      {2, 128, 128, 64, 0, &launch_w64<_Float16, false, 2>, 2},
+                                      {2, 128, 128, 64, 1, &launch_w64<_Float16, true, 2>, 2}};
 #endif
 
 }  // namespace fa

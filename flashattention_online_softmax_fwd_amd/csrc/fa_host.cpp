@@ -46,14 +46,23 @@ const fa::KernelEntry* table_for(int dtype, int* n)
     }
 }
 
-const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n)
+// units: B * Hq (query heads of the batch), N: query rows per head; they size the grid when the
+// default tile depends on it.
+const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n, long long units = 0,
+                                   long long N = 0)
 {
-    // 16-bit inputs at d = 128: the 64-rows-per-wave kernel serves the default 128 x 64 tile
-    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128 &&
-        ((block_m == 0 && block_n == 0) || (block_m == 128 && block_n == 64))) {
+    // 16-bit inputs at d = 128: the 64-rows-per-wave kernels serve the 256 x 64 and 128 x 64 tiles
+    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128) {
         const fa::KernelEntry* w = dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels;
+        if (block_m == 0 && block_n == 0) {
+            // 256-row workgroups when the grid gives every CU at least two of them, else 128-row
+            // ones (twice the workgroups for small grids)
+            const uint64_t wg256 = (uint64_t)units * (((uint64_t)N + 255) / 256);
+            block_m = wg256 >= 2 * 256 ? 256 : 128;
+            block_n = 64;
+        }
         for (int i = 0; i < fa::kNumW64Kernels; ++i)
-            if (w[i].causal == causal) return &w[i];
+            if (w[i].causal == causal && w[i].block_m == block_m && w[i].block_n == block_n) return &w[i];
     }
     int n = 0;
     const fa::KernelEntry* table = table_for(dtype, &n);
@@ -129,7 +138,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
         overlaps(o, qbytes, lse, lbytes))
         return fail(FA_ERR_INVALID_ARG, "o and lse must not overlap the inputs or each other");
 
-    const fa::KernelEntry* e = find_kernel(dtype, d, causal, block_m, block_n);
+    const fa::KernelEntry* e = find_kernel(dtype, d, causal, block_m, block_n, (long long)B * Hq, N);
     if (!e) {
         char buf[96];
         std::snprintf(buf, sizeof buf, "tile %dx%d not built for this dtype and d", block_m, block_n);
@@ -482,7 +491,7 @@ long long fa_fwd_stamp_slots(int B, int Hq, int N, int d, int dtype)
 {
     if (B < 0 || Hq < 1 || N < 0 || (d != 64 && d != 128)) return -1;
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return -1;
-    const fa::KernelEntry* e = find_kernel(dtype, d, 0, 0, 0);
+    const fa::KernelEntry* e = find_kernel(dtype, d, 0, 0, 0, (long long)B * Hq, N);
     if (!e) return -1;
     return (long long)B * Hq * (((long long)N + e->block_m - 1) / e->block_m) *
            (e->waves ? e->waves : e->block_m / 32);
@@ -544,16 +553,28 @@ int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap)
 {
     if (!known_dtype(dtype)) return -1;
     if (d != 64 && d != 128) return -1;
+    // every distinct (block_m, block_n) that find_kernel can reach, in the order it prefers them
+    int pairs[16][2];
+    int count = 0;
+    auto add = [&](const fa::KernelEntry* t, int n) {
+        for (int i = 0; i < n; ++i) {
+            if (t[i].d != d || t[i].causal != 0) continue;
+            bool seen = false;
+            for (int j = 0; j < count; ++j) seen = seen || (pairs[j][0] == t[i].block_m && pairs[j][1] == t[i].block_n);
+            if (seen || count == 16) continue;
+            pairs[count][0] = t[i].block_m;
+            pairs[count][1] = t[i].block_n;
+            ++count;
+        }
+    };
+    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128)
+        add(dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels, fa::kNumW64Kernels);
     int n = 0;
     const fa::KernelEntry* table = table_for(dtype, &n);
-    int count = 0;
-    for (int i = 0; i < n; ++i) {
-        if (table[i].d != d || table[i].causal != 0) continue;
-        if (count < cap && block_m && block_n) {
-            block_m[count] = table[i].block_m;
-            block_n[count] = table[i].block_n;
-        }
-        ++count;
+    add(table, n);
+    for (int j = 0; j < count && j < cap && block_m && block_n; ++j) {
+        block_m[j] = pairs[j][0];
+        block_n[j] = pairs[j][1];
     }
     return count;
 }

@@ -47,11 +47,11 @@ extern const KernelEntry kF16Kernels[];
 extern const int kNumF16Kernels;
 extern const KernelEntry kF32Kernels[];
 extern const int kNumF32Kernels;
-// The 64-rows-per-wave forward (fa_fwd_w64.hip): d = 128, 128 x 64 tiles, the default for
-// 16-bit inputs at d = 128.
+// The 64-rows-per-wave forward (fa_fwd_w64.hip): d = 128, 128 x 64 tiles (2 waves) and
+// 256 x 64 tiles (4 waves); the default for 16-bit inputs at d = 128 comes first.
 extern const KernelEntry kBf16W64Kernels[];
 extern const KernelEntry kF16W64Kernels[];
-constexpr int kNumW64Kernels = 2;
+constexpr int kNumW64Kernels = 4;
 // Split-KV partial-state kernels (16-bit inputs, float partial outputs).
 extern const KernelEntry kBf16SplitKernels[];
 extern const int kNumBf16SplitKernels;

@@ -41,7 +41,7 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-OUT = os.path.join(HERE, "fa_fwd_kloop.inc")
+OUT = os.environ.get("OUT_INC") or os.path.join(HERE, "fa_fwd_kloop.inc")
 
 NEG_INF_BITS = "0xff800000"
 
@@ -95,6 +95,19 @@ NVCLOB = 224         # v0..v223 clobbered
 
 def Or(rb, db):
     return 64 * rb + 16 * db
+
+
+# Row sums: "valu" adds the fp32 P with vector adds (the default: measured faster); "mfma"
+# adds P over the keys with one more product per 16 keys and row block whose A operand is all
+# ones (l then sits in AGPRs beside O and sums the rounded P), 2-5% slower on the causal
+# d = 128 workloads: the extra eighth of matrix work costs more than the vector adds it saves.
+ROWSUM = os.environ.get("FA_GEN_ROWSUM", "valu")
+ONES = 216           # v216..v219: the all-ones A operand of the row-sum products
+
+
+def Lacc(rb):
+    """AGPRs of the row-sum product of row block rb (every register holds l of the lane's row)."""
+    return 128 + 16 * rb
 
 
 # ---------------------------------------------------------------- instructions
@@ -213,6 +226,8 @@ def emit(ins, st, out):
     if ins.kind == "label":
         out.append(ins.text)
         return
+    if ins.kind == "waitall":
+        st.lds = []
     touched = [(r, "use") for r in ins.uses] + [(r, "def") for r in ins.defs]
     # LDS reads still in flight whose destination this instruction touches
     if st.lds:
@@ -346,6 +361,13 @@ class Gen:
             out.append(([self.k_read(st, kk, t)], prods))
         return out
 
+    def mfma_l(self, pbuf, rb, ks):
+        a = Lacc(rb)
+        uses = regs(ONES, 4) + regs(Pr(pbuf, rb, ks), 4) + regs(a, 16, "a")
+        return Ins("%s a[%d:%d], %s, %s, a[%d:%d]" % (self.mfma_op, a, a + 15, vrange(ONES, 4),
+                                                      vrange(Pr(pbuf, rb, ks), 4), a, a + 15),
+                   "mfma", defs=regs(a, 16, "a"), uses=uses, srcc=set(regs(a, 16, "a")))
+
     def pv_stream(self, pbuf, t, rbs):
         out = []
         n = 0
@@ -355,6 +377,8 @@ class Gen:
                 n += 1
                 prods = [self.mfma_pv(pbuf, rb, db, ks, st) for rb in rbs]
                 out.append((self.v_reads(st, db, ks, t), prods))
+            if ROWSUM == "mfma":
+                out.append(([], [self.mfma_l(pbuf, rb, ks) for rb in rbs]))
         return out
 
 
@@ -385,7 +409,7 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
         mask_sgpr = mask_sgprs[rb]
         o = streams[rb]
         s = Sr(sbuf, rb)
-        base = 12 * idx      # temporaries of this row block: t(base) .. t(base + 11)
+        base = 8 * idx       # temporaries of this row block: t(base) .. t(base + 8)
         T = lambda n: vr(t(base + n))
         m = masks.get(rb)
         if m:
@@ -450,6 +474,15 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
             pe.append(Ins("v_fma_f32 %s, %s, %%[c], -%s" % (S(r), S(r), ref), "valu", defs=[S(r)], uses=[S(r), ref]))
             pe.append(Ins("v_exp_f32_e32 %s, %s" % (S(r), S(r)), "trans", defs=[S(r)], uses=[S(r)]))
         o.extend(pe)
+        cvts = []
+        for ks in range(2):
+            for j in range(4):
+                p = Pr(pbuf, rb, ks) + j
+                cvts.append(Ins("%s %s, %s, %s" % (g.cvt_op, vr(p), S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)), "valu",
+                                defs=[vr(p)], uses=[S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)]))
+        if ROWSUM == "mfma":
+            o.extend(cvts)
+            continue
         sums = []
         for c in range(4):
             sums.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + c), S(2 * c), S(2 * c + 1)), "valu",
@@ -458,12 +491,6 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
             c = r % 4
             sums.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + c), S(r), T(5 + c)), "valu", defs=[T(5 + c)],
                             uses=[S(r), T(5 + c)]))
-        cvts = []
-        for ks in range(2):
-            for j in range(4):
-                p = Pr(pbuf, rb, ks) + j
-                cvts.append(Ins("%s %s, %s, %s" % (g.cvt_op, vr(p), S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)), "valu",
-                                defs=[vr(p)], uses=[S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)]))
         # interleave sums and conversions
         for a, b in zip(sums[:8], cvts):
             o.append(a)
@@ -496,6 +523,8 @@ def rescale_block(par, rbs):
     """O *= alpha[par] on the row blocks rbs: read, multiply, write back, 8 at a time."""
     out = [Ins("s_nop 7", "nop")]
     regs_list = [(rb, Or(rb, db) + r) for rb in rbs for db in range(4) for r in range(16)]
+    if ROWSUM == "mfma":
+        regs_list += [(rb, Lacc(rb) + r) for rb in rbs for r in range(16)]
     for i in range(0, len(regs_list), 8):
         chunk = regs_list[i:i + 8]
         for j, (rb, a) in enumerate(chunk):
@@ -508,29 +537,36 @@ def rescale_block(par, rbs):
     return out
 
 
-def merge_half(prod_streams, valu, extra, lead=2):
+def merge_half(prod_streams, valu, extra, lead=2, preissued=0, head_valu=0, next_reads=()):
     """Interleave one half: the product streams (list of (reads, products) in order), the
     vector work and the extra instructions (DMA, toggles).  Each group's reads are issued
     ``lead`` groups ahead of its products; the vector and extra work is spread evenly over
-    the products."""
+    the products.  ``preissued``: the first groups whose reads the previous half already
+    issued; ``head_valu``: vector instructions placed between the first reads and the first
+    product (work that covers the read latency); ``next_reads``: the next half's first reads,
+    issued after this half's last reads."""
     groups = []
     for stream in prod_streams:
         groups.extend(stream)
     nprod = sum(len(p) for _, p in groups)
     out = []
-    # initial reads
-    for k in range(min(lead, len(groups))):
+    for k in range(preissued, min(lead, len(groups))):
         out.extend(groups[k][0])
-    vi = 0
+    vi = h0 = min(head_valu, len(valu))
+    out.extend(valu[:vi])
     ei = 0
     done = 0
+    pending_next = list(next_reads)
     for gi, (_, prods) in enumerate(groups):
         if gi + lead < len(groups):
             out.extend(groups[gi + lead][0])
+        elif pending_next:
+            out.extend(pending_next)
+            pending_next = []
         for p in prods:
             out.append(p)
             done += 1
-            vt = (len(valu) * done + nprod - 1) // nprod if nprod else len(valu)
+            vt = h0 + ((len(valu) - h0) * done + nprod - 1) // nprod if nprod else len(valu)
             et = (len(extra) * done + nprod - 1) // nprod if nprod else len(extra)
             while ei < et:
                 out.append(extra[ei])
@@ -538,6 +574,7 @@ def merge_half(prod_streams, valu, extra, lead=2):
             while vi < vt:
                 out.append(valu[vi])
                 vi += 1
+    out.extend(pending_next)
     out.extend(extra[ei:])
     out.extend(valu[vi:])
     return out
@@ -545,15 +582,16 @@ def merge_half(prod_streams, valu, extra, lead=2):
 
 # ---------------------------------------------------------------- tile loads (LDS DMA)
 
-def dma_tile(which):
-    """This wave's half of one 64-key K or V tile: 8 slices of 1 KiB, slice ii = wave + 2i,
-    from %[<which>src] (byte offset of the tile in the head) into the buffer at
-    %[<which>dst] (LDS address of this wave's first slice in the tile's buffer)."""
+def dma_tile(which, nw):
+    """This wave's share of one 64-key K or V tile (16 slices of 1 KiB, slice ii = wave + nw*i)
+    from %[<which>src] (byte offset of the tile in the head) into the buffer at %[<which>dst]
+    (LDS address of this wave's first slice in the tile's buffer).  The lane's source offset
+    within a slice depends on ii only through ii mod 4: %[dma0] (i even) and %[dma1] (i odd)."""
     out = []
     rs = "%[krs]" if which == "k" else "%[vrs]"
-    for i in range(8):
-        out.append(Ins("s_add_u32 m0, %%[%sdst], %d" % (which, 2048 * i), "m0", defs=["m0"]))
-        out.append(Ins("s_add_u32 %%[soff], %%[%ssrc], %d" % (which, 2048 * i), "salu", defs=["%[soff]"]))
+    for i in range(16 // nw):
+        out.append(Ins("s_add_u32 m0, %%[%sdst], %d" % (which, 1024 * nw * i), "m0", defs=["m0"]))
+        out.append(Ins("s_add_u32 %%[soff], %%[%ssrc], %d" % (which, 1024 * nw * i), "salu", defs=["%[soff]"]))
         out.append(Ins("buffer_load_dwordx4 %%[dma%d], %s, %%[soff] offen lds" % (i & 1, rs), "dma",
                        uses=["m0", "%[soff]"]))
     return out
@@ -583,15 +621,15 @@ def toggle_reads():
 
 
 def barrier():
-    return [Ins("s_waitcnt vmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
+    """Every wave's tile loads have landed and its LDS reads have returned; then the barrier.
+    (Loads that write LDS directly count in vmcnt, and a barrier does not wait for them.)"""
+    return [Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "waitall"), Ins("s_barrier", "barrier")]
 
 
 # ---------------------------------------------------------------- the program
 
-def half_interleaved(g, s_next, pv_prev, soft, rescale_par, extra=()):
-    """One half with the S and PV products alternating (used when no rescale can intervene
-    between them: the rescale for the previous half is applied before this half starts)."""
-    ps = []
+def half_groups(g, s_next, pv_prev):
+    """The product groups of one half, S and PV alternating."""
     s_groups = g.s_stream(*s_next) if s_next else []
     pv_groups = g.pv_stream(*pv_prev) if pv_prev else []
     merged = []
@@ -600,15 +638,41 @@ def half_interleaved(g, s_next, pv_prev, soft, rescale_par, extra=()):
             merged.append(s_groups[i])
         if i < len(pv_groups):
             merged.append(pv_groups[i])
+    return merged
+
+
+LEAD = 2          # product groups a group's operand reads run ahead
+HEAD_VALU = 12    # softmax instructions that cover the first reads of a half after a barrier
+
+
+def first_reads(g, s_next, pv_prev):
+    """The reads of a half's first LEAD groups (to be issued by the half before it)."""
     out = []
-    if pv_groups and rescale_par is not None:
-        out.append(Skip("%%[ga%d]" % rescale_par, rescale_block(rescale_par, pv_prev[2]), "L_rs%d" % len(g.labels)))
-        g.labels.append(1)
-    out.extend(merge_half([merged], list(soft), list(extra)))
+    for reads, _ in half_groups(g, s_next, pv_prev)[:LEAD]:
+        out.extend(reads)
     return out
 
 
-def build(elem, causal):
+def half_interleaved(g, s_next, pv_prev, soft, rescale_par, extra=(), preissued=False, next_half=None,
+                     after_barrier=False):
+    """One half with the S and PV products alternating.  The rescale of O for the previous
+    half's softmax, when any row moved its reference, comes before the first product.
+    preissued: this half's first reads were issued by the previous half; next_half:
+    (s_next, pv_prev) of the following half when no barrier separates them, whose first
+    reads this half issues at its end; after_barrier: start with a few softmax
+    instructions while the first reads are in flight."""
+    merged = half_groups(g, s_next, pv_prev)
+    out = []
+    if pv_prev and rescale_par is not None:
+        out.append(Skip("%%[ga%d]" % rescale_par, rescale_block(rescale_par, pv_prev[2]), "L_rs%d" % len(g.labels)))
+        g.labels.append(1)
+    nxt = first_reads(g, *next_half) if next_half else ()
+    out.extend(merge_half([merged], list(soft), list(extra), lead=LEAD, preissued=LEAD if preissued else 0,
+                          head_valu=HEAD_VALU if after_barrier else 0, next_reads=nxt))
+    return out
+
+
+def build(elem, causal, nw):
     g = Gen(elem, causal)
     g.labels = []
     all_rb = (0, 1)
@@ -625,17 +689,21 @@ def build(elem, causal):
             base = "%[qoff]" if rb == 0 else vr(t(0))
             prog.append(Ins("buffer_load_dwordx4 %s, %s, %%[qrs], 0 offen offset:%d" % (vrange(Qr(rb, kk), 4), base, 32 * kk),
                             "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else [vr(t(0))]))
-    for a in range(128):
+    for a in range(160 if ROWSUM == "mfma" else 128):
         prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
+    if ROWSUM == "mfma":
+        one2 = "0x3f803f80" if elem == "bf16" else "0x3c003c00"
+        for i in range(4):
+            prog.append(Ins("v_mov_b32 %s, %s" % (vr(ONES + i), one2), "valu", defs=[vr(ONES + i)]))
     prog.append(Ins("s_waitcnt vmcnt(0)", "wait"))
     for r in range(64):
         prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
     # ---- first tiles: K(0), K(1) (if any), V(0)
-    prog.extend(dma_tile("k"))
+    prog.extend(dma_tile("k", nw))
     prog.extend(advance_k())
-    prog.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k"), "L_k1"))
+    prog.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k", nw), "L_k1"))
     prog.extend(advance_k())
-    prog.extend(dma_tile("v"))
+    prog.extend(dma_tile("v", nw))
     prog.extend(advance_v())
     prog.extend(barrier())
     # S(0) alone
@@ -653,8 +721,8 @@ def build(elem, causal):
     def iter_head(cond_k, cond_v):
         out = toggle_reads()
         out.extend(barrier())
-        ek = dma_tile("k") + advance_k()
-        ev = dma_tile("v") + advance_v()
+        ek = dma_tile("k", nw) + advance_k()
+        ev = dma_tile("v", nw) + advance_v()
         if cond_k:
             ek = [Cond(["s_add_u32 %[soff], %[kit], 1", "s_cmp_lt_u32 %[soff], %[nt]"], ek, "L_ck%d" % len(g.labels))]
             g.labels.append(1)
@@ -672,20 +740,22 @@ def build(elem, causal):
     head, dmas = iter_head(False, False)
     body = list(head)
     body.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
-                                 softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas))
+                                 softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas,
+                                 next_half=((1, 1, all_rb), (1, 1, all_rb)), after_barrier=True))
     body.extend(half_interleaved(g, (1, 1, all_rb), (1, 1, all_rb),
-                                 softmax_ops(g, 0, 0, 0, {}, False, ()), 1, []))
+                                 softmax_ops(g, 0, 0, 0, {}, False, ()), 1, [], preissued=True))
     body.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     pathA.append(Ins("s_sub_u32 %[cnt], %[last], 1", "salu", defs=["%[cnt]"]))
     pathA.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", body, "L_loop")], "L_skiploop"))
     # iteration L: half 2L-1 unmasked, half 2L masked A
     head, dmas = iter_head(True, False)
     pathA.extend(head)
-    pathA.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
-                                  softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas))
     pathA.extend(lim_ops("limA"))
+    pathA.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
+                                  softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas,
+                                  next_half=((1, 1, rbB), (1, 1, all_rb)), after_barrier=True))
     pathA.extend(half_interleaved(g, (1, 1, rbB), (1, 1, all_rb),
-                                  softmax_ops(g, 0, 0, 0, maskA, False, ()), 1, []))
+                                  softmax_ops(g, 0, 0, 0, maskA, False, ()), 1, [], preissued=True))
     pathA.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     pathA.append(Ins("s_branch L_tailB_%=", "branch"))
     # ---- L == 0 path: half 0 masked A
@@ -700,8 +770,9 @@ def build(elem, causal):
     tail.extend(head)
     tail.extend(lim_ops("limB"))
     tail.extend(half_interleaved(g, None, (0, 0, all_rb),
-                                 softmax_ops(g, 1, 1, 1, maskB, False, deadB), 0, dmas))
-    tail.extend(half_interleaved(g, None, (1, 1, rbB), [], 1, []))
+                                 softmax_ops(g, 1, 1, 1, maskB, False, deadB), 0, dmas,
+                                 next_half=(None, (1, 1, rbB)), after_barrier=True))
+    tail.extend(half_interleaved(g, None, (1, 1, rbB), [], 1, [], preissued=True))
     tail.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     # the wave is done with its rows: store O and LSE
     tail.extend(epilogue(g))
@@ -722,10 +793,13 @@ def epilogue(g):
     out = [Ins("s_nop 15", "nop"), Ins("s_nop 15", "nop")]
     for rb in (0, 1):
         L = vr(Lr(rb))
-        tl = vr(t(20))
-        out.append(Ins("v_mov_b32_e32 %s, %s" % (tl, L), "valu", defs=[tl], uses=[L]))
-        out.append(Ins("v_permlane32_swap_b32_e32 %s, %s" % (L, tl), "perm", defs=[L, tl], uses=[L, tl]))
-        out.append(Ins("v_add_f32_e32 %s, %s, %s" % (L, L, tl), "valu", defs=[L], uses=[L, tl]))
+        if ROWSUM == "mfma":
+            out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (L, Lacc(rb)), "accr", defs=[L], uses=["a%d" % Lacc(rb)]))
+        else:
+            tl = vr(t(20))
+            out.append(Ins("v_mov_b32_e32 %s, %s" % (tl, L), "valu", defs=[tl], uses=[L]))
+            out.append(Ins("v_permlane32_swap_b32_e32 %s, %s" % (L, tl), "perm", defs=[L, tl], uses=[L, tl]))
+            out.append(Ins("v_add_f32_e32 %s, %s, %s" % (L, L, tl), "valu", defs=[L], uses=[L, tl]))
         inv = vr(t(21))
         out.append(Ins("v_rcp_f32_e32 %s, %s" % (inv, L), "trans", defs=[inv], uses=[L]))
         lg = vr(t(22))
@@ -758,8 +832,8 @@ def epilogue(g):
     return out
 
 
-def assemble(elem, causal):
-    g, prog, pathA, pathB, tail = build(elem, causal)
+def assemble(elem, causal, nw):
+    g, prog, pathA, pathB, tail = build(elem, causal, nw)
     st = State()
     out = []
     lower(prog, st, out, "%=")
@@ -782,13 +856,15 @@ def c_string(lines):
 
 def main():
     parts = ["// Generated by gen_fwd_kloop.py; do not edit.  The key loop of the 64-rows-per-wave\n"
-             "// forward (fa_fwd_w64.hip) as gfx950 assembly, one string per element type and mask.\n"
+             "// forward (fa_fwd_w64.hip) as gfx950 assembly, one string per element type, mask and\n"
+             "// number of waves per workgroup (which share each tile's loads).\n"
              "#pragma once\n"]
-    for elem in ("bf16", "f16"):
-        for causal in (False, True):
-            lines = assemble(elem, causal)
-            name = "FA_KLOOP_%s_%s" % (elem.upper(), "CAUSAL" if causal else "FULL")
-            parts.append("#define %s \\\n%s\n" % (name, " \\\n".join('    "%s\\n"' % l for l in lines)))
+    for nw in (2, 4):
+        for elem in ("bf16", "f16"):
+            for causal in (False, True):
+                lines = assemble(elem, causal, nw)
+                name = "FA_KLOOP_%s_%s_W%d" % (elem.upper(), "CAUSAL" if causal else "FULL", nw)
+                parts.append("#define %s \\\n%s\n" % (name, " \\\n".join('    "%s\\n"' % l for l in lines)))
     text = "\n".join(parts)
     with open(OUT, "w") as f:
         f.write(text)

@@ -10,6 +10,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -91,3 +92,36 @@ def test_static_workspace_is_a_device_symbol(bwd_asm):
     assert m, "no global device symbol for the static workspace"
     size = re.search(r"^\s*\.size\s+%s,\s*(\d+)" % re.escape(m.group(1)), bwd_asm, re.M)
     assert size and int(size.group(1)) == 128 << 20
+
+
+@pytest.fixture(scope="module")
+def w64_asm(tmp_path_factory):
+    return compile_asm(tmp_path_factory, "fa_fwd_w64.hip")
+
+
+def test_w64_kernels_wait_for_lds_dma_before_barriers_and_do_not_spill(w64_asm):
+    """The 64-rows-per-wave forward is written as assembly by gen_fwd_kloop.py: every barrier
+    must still follow a wait for this wave's LDS DMA loads (vmcnt(0)), and the kernels must
+    fit the register file (one wave per SIMD) without scratch."""
+    found = 0
+    for name, ins in kernels(w64_asm, r"_ZN2fa14fwd_w64_kernel"):
+        found += 1
+        assert any(x.startswith("buffer_load_dwordx4") and x.endswith("lds") for x in ins), name
+        for n, x in enumerate(ins):
+            if x.startswith("s_barrier"):
+                assert ins[n - 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[n - 1], (name, n, ins[n - 1])
+        assert not any(x.startswith(("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")) for x in ins), name
+        assert not any(x.startswith("scratch_") for x in ins), name
+        assert not any(x.startswith(("s_store", "s_buffer_store", "s_atomic", "s_dcache")) for x in ins), name
+    assert found == 8       # bf16 and fp16, causal or not, 2 or 4 waves
+
+
+def test_generated_key_loop_is_up_to_date():
+    """fa_fwd_kloop.inc is what gen_fwd_kloop.py writes (the build regenerates it)."""
+    import tempfile
+    gen = os.path.join(CSRC, "gen_fwd_kloop.py")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.inc")
+        env = dict(os.environ, OUT_INC=out)
+        subprocess.run([sys.executable, gen], check=True, env=env)
+        assert open(out).read() == open(os.path.join(CSRC, "fa_fwd_kloop.inc")).read()
