@@ -97,17 +97,22 @@ def Or(rb, db):
     return 64 * rb + 16 * db
 
 
-# Row sums: "valu" adds the fp32 P with vector adds (the default: measured faster); "mfma"
-# adds P over the keys with one more product per 16 keys and row block whose A operand is all
-# ones (l then sits in AGPRs beside O and sums the rounded P), 2-5% slower on the causal
-# d = 128 workloads: the extra eighth of matrix work costs more than the vector adds it saves.
+# Row sums: "valu" adds the fp32 P with vector adds (the default); "mfma16" adds the rounded
+# P with one 16x16x32 product per 16 keys and row block, whose 0/1 A operand makes every
+# lane's four results the sum over both lane halves of the lane's own row (see ones16), so l
+# sits in AGPRs beside O.  Measured equal on the causal d = 128 workloads (64 vector adds per
+# tile traded for 8 small products); an all-ones 32x32x16 product instead was 2-5% slower.
 ROWSUM = os.environ.get("FA_GEN_ROWSUM", "valu")
-ONES = 216           # v216..v219: the all-ones A operand of the row-sum products
+if ROWSUM not in ("valu", "mfma16"):
+    raise SystemExit("FA_GEN_ROWSUM must be valu or mfma16")
+ONES = 216           # v216..v219: the 0/1 A operand of the row-sum products
+MFMA_ROWSUM = ROWSUM == "mfma16"
+LACC_REGS = 4
 
 
 def Lacc(rb):
     """AGPRs of the row-sum product of row block rb (every register holds l of the lane's row)."""
-    return 128 + 16 * rb
+    return 128 + LACC_REGS * rb
 
 
 # ---------------------------------------------------------------- instructions
@@ -319,6 +324,12 @@ class Gen:
         self.elem = elem            # "bf16" or "f16"
         self.causal = causal
         self.mfma_op = "v_mfma_f32_32x32x16_" + elem
+        self.mfma16_op = "v_mfma_f32_16x16x32_" + elem
+        # How far (log2 units) a row's maximum may rise above its reference before O, l
+        # and the reference are rescaled.  P = exp2(S c - m) then stays below 2^slack: bf16
+        # has float32's exponent range, so 2^48 is exact and O's float32 sums stay finite
+        # while N * max|v| < 2^80; fp16 P must stay below 65504, hence 15.
+        self.slack = "0x42400000" if elem == "bf16" else "0x41700000"     # 48.0, 15.0
         self.cvt_op = "v_cvt_pk_bf16_f32" if elem == "bf16" else "v_cvt_pk_f16_f32"
 
     # ---- operand reads from LDS
@@ -363,10 +374,12 @@ class Gen:
 
     def mfma_l(self, pbuf, rb, ks):
         a = Lacc(rb)
-        uses = regs(ONES, 4) + regs(Pr(pbuf, rb, ks), 4) + regs(a, 16, "a")
-        return Ins("%s a[%d:%d], %s, %s, a[%d:%d]" % (self.mfma_op, a, a + 15, vrange(ONES, 4),
-                                                      vrange(Pr(pbuf, rb, ks), 4), a, a + 15),
-                   "mfma", defs=regs(a, 16, "a"), uses=uses, srcc=set(regs(a, 16, "a")))
+        n = LACC_REGS
+        op = self.mfma16_op
+        uses = regs(ONES, 4) + regs(Pr(pbuf, rb, ks), 4) + regs(a, n, "a")
+        return Ins("%s a[%d:%d], %s, %s, a[%d:%d]" % (op, a, a + n - 1, vrange(ONES, 4),
+                                                      vrange(Pr(pbuf, rb, ks), 4), a, a + n - 1),
+                   "mfma", defs=regs(a, n, "a"), uses=uses, srcc=set(regs(a, n, "a")))
 
     def pv_stream(self, pbuf, t, rbs):
         out = []
@@ -377,7 +390,7 @@ class Gen:
                 n += 1
                 prods = [self.mfma_pv(pbuf, rb, db, ks, st) for rb in rbs]
                 out.append((self.v_reads(st, db, ks, t), prods))
-            if ROWSUM == "mfma":
+            if MFMA_ROWSUM:
                 out.append(([], [self.mfma_l(pbuf, rb, ks) for rb in rbs]))
         return out
 
@@ -450,7 +463,7 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
         o.append(Ins("v_max_f32_e32 %s, %s, %s" % (T(0), T(0), T(1)), "valu", defs=[T(0)], uses=[T(0), T(1)]))
         # scaled max, lazy move of the reference (only past 2^8 of growth)
         o.append(Ins("v_mul_f32_e32 %s, %%[c], %s" % (T(0), T(0)), "valu", defs=[T(0)], uses=[T(0)]))
-        o.append(Ins("v_add_f32_e32 %s, 0x41000000, %s" % (T(2), vr(Mr(rb))), "valu", defs=[T(2)], uses=[vr(Mr(rb))]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(2), g.slack, vr(Mr(rb))), "valu", defs=[T(2)], uses=[vr(Mr(rb))]))
         gb = "%%[g%d%d]" % (par, rb)
         o.append(Ins("v_cmp_gt_f32_e64 %s, %s, %s" % (gb, T(0), T(2)), "cmps", defs=[gb], uses=[T(0), T(2)]))
         o.append(Ins("v_cndmask_b32_e64 %s, %s, %s, %s" % (T(3), vr(Mr(rb)), T(0), gb), "valu", defs=[T(3)],
@@ -480,7 +493,7 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
                 p = Pr(pbuf, rb, ks) + j
                 cvts.append(Ins("%s %s, %s, %s" % (g.cvt_op, vr(p), S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)), "valu",
                                 defs=[vr(p)], uses=[S(8 * ks + 2 * j), S(8 * ks + 2 * j + 1)]))
-        if ROWSUM == "mfma":
+        if MFMA_ROWSUM:
             o.extend(cvts)
             continue
         sums = []
@@ -523,8 +536,8 @@ def rescale_block(par, rbs):
     """O *= alpha[par] on the row blocks rbs: read, multiply, write back, 8 at a time."""
     out = [Ins("s_nop 7", "nop")]
     regs_list = [(rb, Or(rb, db) + r) for rb in rbs for db in range(4) for r in range(16)]
-    if ROWSUM == "mfma":
-        regs_list += [(rb, Lacc(rb) + r) for rb in rbs for r in range(16)]
+    if MFMA_ROWSUM:
+        regs_list += [(rb, Lacc(rb) + r) for rb in rbs for r in range(LACC_REGS)]
     for i in range(0, len(regs_list), 8):
         chunk = regs_list[i:i + 8]
         for j, (rb, a) in enumerate(chunk):
@@ -689,12 +702,10 @@ def build(elem, causal, nw):
             base = "%[qoff]" if rb == 0 else vr(t(0))
             prog.append(Ins("buffer_load_dwordx4 %s, %s, %%[qrs], 0 offen offset:%d" % (vrange(Qr(rb, kk), 4), base, 32 * kk),
                             "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else [vr(t(0))]))
-    for a in range(160 if ROWSUM == "mfma" else 128):
+    for a in range(128 + 2 * LACC_REGS if MFMA_ROWSUM else 128):
         prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
-    if ROWSUM == "mfma":
-        one2 = "0x3f803f80" if elem == "bf16" else "0x3c003c00"
-        for i in range(4):
-            prog.append(Ins("v_mov_b32 %s, %s" % (vr(ONES + i), one2), "valu", defs=[vr(ONES + i)]))
+    if MFMA_ROWSUM:
+        prog.extend(ones16(elem))
     prog.append(Ins("s_waitcnt vmcnt(0)", "wait"))
     for r in range(64):
         prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
@@ -789,11 +800,37 @@ def build(elem, causal, nw):
     return g, prog, pathA, pathB, tail
 
 
+def ones16(elem):
+    """The A operand of the 16x16x32 row-sum products.
+
+    P of a row block sits as the B operand of a 32x32x16 product: lane L holds row L % 32 and
+    8 keys.  Read as the B operand of a 16x16x32 product, lane L is column L % 16 in k-group
+    L // 16, so column n gathers rows n (groups 0, 2) and n + 16 (groups 1, 3).  With
+    A[m][k] = 1 exactly when the k-group's parity equals bit 2 of m, output row m sums the 16
+    keys of row n + 16 * ((m >> 2) & 1); the 16x16 output puts rows 4 * (L // 16) + j in
+    lane L, so every result of lane L is the sum over the keys of row L % 32, its own row.
+    Lane L of A is row L % 16, k-group L // 16: one when bit 4 of L equals bit 2 of L."""
+    one2 = "0x3f803f80" if elem == "bf16" else "0x3c003c00"
+    a, b, c = vr(t(1)), vr(t(2)), vr(t(3))
+    out = [Ins("v_mbcnt_lo_u32_b32 %s, -1, 0" % a, "valu", defs=[a]),
+           Ins("v_mbcnt_hi_u32_b32 %s, -1, %s" % (a, a), "valu", defs=[a], uses=[a]),
+           Ins("v_lshrrev_b32_e32 %s, 2, %s" % (b, a), "valu", defs=[b], uses=[a]),
+           Ins("v_lshrrev_b32_e32 %s, 4, %s" % (a, a), "valu", defs=[a], uses=[a]),
+           Ins("v_xor_b32_e32 %s, %s, %s" % (a, a, b), "valu", defs=[a], uses=[a, b]),
+           Ins("v_and_b32_e32 %s, 1, %s" % (a, a), "valu", defs=[a], uses=[a]),
+           Ins("v_mov_b32_e32 %s, %s" % (c, one2), "valu", defs=[c]),
+           Ins("v_cmp_eq_u32_e32 vcc, 0, %s" % a, "cmps", defs=["vcc"], uses=[a])]
+    for i in range(4):
+        out.append(Ins("v_cndmask_b32_e32 %s, 0, %s, vcc" % (vr(ONES + i), c), "valu",
+                       defs=[vr(ONES + i)], uses=[c, "vcc"]))
+    return out
+
+
 def epilogue(g):
     out = [Ins("s_nop 15", "nop"), Ins("s_nop 15", "nop")]
     for rb in (0, 1):
         L = vr(Lr(rb))
-        if ROWSUM == "mfma":
+        if MFMA_ROWSUM:
             out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (L, Lacc(rb)), "accr", defs=[L], uses=["a%d" % Lacc(rb)]))
         else:
             tl = vr(t(20))

@@ -89,6 +89,11 @@ enum {
  *             after scaling, in float32, and beyond that the maximum's own
  *             rounding can overflow the exponentials (a 0 scale gives uniform
  *             weights; a negative one reverses the order of the scores)
+ *   v         values' magnitude: the 16-bit kernels let a row's maximum run up
+ *             to 2^8 (bf16 at d = 128: 2^48) above the reference they subtract
+ *             before moving it, so O's float32 sums reach N * 2^48 * max|v|;
+ *             bf16 inputs at d = 128 need N * max|v| < 2^80, the others
+ *             N * max|v| < 2^120
  *   dtype     FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16
  *   stream    hipStream_t to enqueue on; NULL means the default stream
  *

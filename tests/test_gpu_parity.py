@@ -301,6 +301,40 @@ def test_max_in_the_last_key_tile(fa, oracle):
         check(lse.numpy(), rl, dtype, "LSE last tile max")
 
 
+# climb of the scores from one block of 32 keys to the next, and the scale: each climb
+# (times scale * log2 e) passes the slack the dtype's kernels leave their running reference
+# (fp32: none, the reference follows every tile; fp16: 8 or 15; bf16: 8 or 48), while the
+# fp32 scaled scores stay below 128, where their rounding (2^-18) is within that bar.
+CLIMB = {"f32": (16.0, 0.5), "f16": (16.0, 1.0), "bf16": (40.0, 1.0)}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_reference_moves_every_half_tile(fa, oracle, dtype, causal, d):
+    """Every block of 32 keys holds each offset 0..31 once, on top of a base that climbs by
+    CLIMB[dtype] from block to block: every row's maximum outruns its reference in every
+    block it reads, so the kernel rescales O and l each time.  q is a unit vector, so a score
+    is the first component of its key (bf16 rounds some above 256 to even values; both sides
+    read the rounded inputs)."""
+    B, Hq, Hkv, N = 1, 2, 2, 300
+    climb, scale = CLIMB[dtype]
+    g = torch.Generator().manual_seed(21)
+    q = torch.zeros(B, Hq, N, d)
+    q[..., 0] = 1.0
+    j = torch.arange(N, dtype=torch.float32)
+    k = torch.zeros(B, Hkv, N, d)
+    k[..., 0] = climb * torch.div(j, 32, rounding_mode="floor") + torch.remainder(j * 7, 32)
+    v = torch.randn((B, Hkv, N, d), generator=g)
+    td = fin.torch_dtype(dtype)
+    q, k, v = q.to(td), k.to(td), v.to(td)
+    o, lse = run_gpu(fa, q, k, v, causal, scale)
+    ro, rl = oracle.attention(q, k, v, causal=causal, scale=scale)
+    tag = "%s causal=%d d=%d" % (dtype, causal, d)
+    check(o.numpy(), ro, dtype, "O climbing scores " + tag)
+    check(lse.numpy(), rl, dtype, "LSE climbing scores " + tag)
+
+
 def test_gqa_equals_repeated_kv_bitwise(fa):
     q, k, v = fin.make_qkv(2, 8, 2, 333, 128, "bf16", 8)
     o1, l1 = run_gpu(fa, q, k, v, True, 0.1)
