@@ -166,6 +166,7 @@ def stamped_clock(w, q, k, v, o, lse):
         return None
     slots = _lib.fa_fwd_stamp_slots(w.B, w.Hq, w.N, w.d, code)
     khz = _lib.fa_wall_clock_khz(q.device.index or 0)
+    simds = 4 * torch.cuda.get_device_properties(q.device).multi_processor_count
     if slots <= 0 or khz <= 0:
         return None
     stamps = torch.zeros(slots * 4, dtype=torch.int64, device=q.device)
@@ -178,13 +179,16 @@ def stamped_clock(w, q, k, v, o, lse):
             raise RuntimeError("fa_fwd_stamped: " + _lib.fa_last_error())
     torch.cuda.synchronize()
     st = stamps.view(slots, 4).cpu().numpy().astype("int64")
+    st = st[st[:, 1] != 0]                 # slots past the launch's waves stay zero
     real = st[:, 1] - st[:, 0]
     cyc = st[:, 3] - st[:, 2]
     span_ticks = int(st[:, 1].max() - st[:, 0].min())
     return {
         "sclk_ghz": float(cyc.sum()) / float(real.sum()) * khz * 1e3 / 1e9,
         "kernel_span_ms": span_ticks / khz,
-        "waves": int(slots),
+        "waves": int(len(st)),
+        # share of SIMD time the waves held: the d = 128 kernels run one wave per SIMD
+        "simd_busy": float(real.sum()) / float(span_ticks * simds) if simds and w.d == 128 else None,
         "wave_ms_mean": float(real.mean()) / khz,
         "wave_ms_max": float(real.max()) / khz,
         "wall_clock_khz": khz,

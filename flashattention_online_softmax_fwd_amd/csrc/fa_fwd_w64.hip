@@ -83,14 +83,49 @@ fwd_w64_kernel(const FwdParams p)
     const int units = p.B * p.Hq;
     const int nqt = p.n_qtiles;
     const int bid = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    unsigned long long real0 = 0, cyc0 = 0;
+    if (p.stamps) {
+        real0 = __builtin_amdgcn_s_memrealtime();
+        cyc0 = __builtin_amdgcn_s_memtime();
+    }
+    // Walk: the workgroup takes pairs j, j + G, ... of the units * ceil(nqt / 2) pairs; pair j
+    // is query tiles nqt - 1 - i and i (i = j mod the pairs per head) of one head, whose
+    // causal work adds up to the same for every i.  With the XCD map, logical workgroup ids
+    // run down each XCD in turn, so the pairs of a head (and of heads sharing K/V) stay in one
+    // L2.  Without the walk, one query tile per workgroup.
+    const int per_head = (nqt + 1) >> 1;
+    int j = 0, jstep = 1, jend = 1;
+    if (p.walk) {
+        const int G = gridDim.x;
+        j = p.xcd_map ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+        jstep = G;
+        jend = units * per_head;
+    }
+#pragma nounroll
+    for (; j < jend; j += jstep)
+#pragma nounroll
+    for (int s = 0; s < 2; ++s) {
     int bh, qt;
-    if (p.xcd_map) {
-        int t;
-        xcd_order(bid, units, nqt, bh, t);
-        qt = CAUSAL ? nqt - 1 - t : t;   // longest first
+    if (p.walk) {
+        bh = j / per_head;
+        const int i = j - bh * per_head;
+        if (s == 1 && i == nqt - 1 - i) break;      // the middle tile of an odd count
+        qt = s == 0 ? nqt - 1 - i : i;
     } else {
-        bh = bid % units;
-        qt = CAUSAL ? nqt - 1 - bid / units : bid / units;
+        if (s == 1) break;
+        if (p.xcd_map) {
+            int t;
+            xcd_order(bid, units, nqt, bh, t);
+            qt = CAUSAL ? nqt - 1 - t : t;   // longest first
+        } else {
+            bh = bid % units;
+            qt = CAUSAL ? nqt - 1 - bid / units : bid / units;
+        }
     }
     const int b = bh / p.Hq;
     const int hk = (bh - b * p.Hq) / p.group;
@@ -105,17 +140,6 @@ fwd_w64_kernel(const FwdParams p)
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, range, 0x00020000);
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)Oh, (short)0, range, 0x00020000);
     const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)Lh, (short)0, N * 4, 0x00020000);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-    unsigned long long real0 = 0, cyc0 = 0;
-    if (p.stamps) {
-        real0 = __builtin_amdgcn_s_memrealtime();
-        cyc0 = __builtin_amdgcn_s_memtime();
-    }
 
     const int q0 = qt * BM;
     const int row0 = q0 + 64 * wave;                    // the wave's first query row
@@ -207,6 +231,9 @@ fwd_w64_kernel(const FwdParams p)
         }
     }
 #undef FA_W64_ASM
+    // every wave is done with the LDS tiles before the next item loads its own
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 
     if (p.stamps && lane == 0) {
         const unsigned long long cyc1 = __builtin_amdgcn_s_memtime();
@@ -227,15 +254,65 @@ FA_W64_INSTANTIATE(4)
 #if !defined(__HIP_DEVICE_COMPILE__)
 namespace {
 
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// 256-row workgroups walk pairs of query tiles: one workgroup per CU at most (each holds a
+// whole CU: one wave per SIMD), as many as give every workgroup the same number of pairs, a
+// multiple of 8 (whole groups of the XCD map).  0 (one tile per workgroup) when the tiles fit
+// on the CUs at once, or when whole pairs would balance worse than single tiles: the walk's
+// critical path is its rounds of pairs (a causal pair is ntiles + 1 tile-rows of work, a
+// non-causal one two tiles), the other's the larger of an even share and the largest tile.
+long long w64_walk_blocks(long long units, long long ntiles, int causal)
+{
+    const int cus = device_cus();
+    if (cus <= 0 || units * ntiles <= cus) return 0;
+    const long long pairs = units * ((ntiles + 1) / 2);
+    const long long rounds = (pairs + cus - 1) / cus;
+    double walk, tiles;
+    if (causal) {
+        walk = (double)rounds * (double)(ntiles + 1);
+        tiles = (double)units * (double)ntiles * (double)(ntiles + 1) / 2.0 / cus;
+        if (tiles < (double)ntiles) tiles = (double)ntiles;
+    } else {
+        walk = 2.0 * (double)rounds;
+        tiles = (double)((units * ntiles + cus - 1) / cus);
+    }
+    if (walk > 1.03 * tiles) return 0;
+    long long g = (pairs + rounds - 1) / rounds;
+    if (cus % 8 == 0) g = (g + 7) / 8 * 8;
+    return g;
+}
+
 template <typename E, bool CAUSAL, int NW>
 hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
 {
     const long long units = (long long)p.B * p.Hq;
     FwdParams args = p;
-    args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
+    long long grid = units * p.n_qtiles;
+    const long long walk = NW == 4 ? w64_walk_blocks(units, p.n_qtiles, CAUSAL) : 0;
+    if (walk > 0) {
+        grid = walk;
+        args.walk = 1;
+        args.xcd_map = (walk % 8 == 0) ? 1 : 0;
+    } else {
+        args.walk = 0;
+        args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
+    }
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL, NW>, dim3((unsigned)(units * p.n_qtiles)),
-                           dim3(64 * NW), kargs, 0, stream);
+    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL, NW>, dim3((unsigned)grid), dim3(64 * NW),
+                           kargs, 0, stream);
 }
 
 }  // namespace
@@ -243,12 +320,12 @@ hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
 // 256-row workgroups first: one K/V tile load per CU instead of two (2-3% faster on the causal
 // d = 128 workloads); the host falls back to 128-row workgroups for grids too small to give
 // every CU two of them.
-const KernelEntry kBf16W64Kernels[] = {{1, 128, 256, 64, 0, &launch_w64<__bf16, false, 4>, 4},
-                                       {1, 128, 256, 64, 1, &launch_w64<__bf16, true, 4>, 4},
+const KernelEntry kBf16W64Kernels[] = {{1, 128, 256, 64, 0, &launch_w64<__bf16, false, 4>, 4, &w64_walk_blocks},
+                                       {1, 128, 256, 64, 1, &launch_w64<__bf16, true, 4>, 4, &w64_walk_blocks},
                                        {1, 128, 128, 64, 0, &launch_w64<__bf16, false, 2>, 2},
                                        {1, 128, 128, 64, 1, &launch_w64<__bf16, true, 2>, 2}};
-const KernelEntry kF16W64Kernels[] = {{2, 128, 256, 64, 0, &launch_w64<_Float16, false, 4>, 4},
-                                      {2, 128, 256, 64, 1, &launch_w64<_Float16, true, 4>, 4},
+const KernelEntry kF16W64Kernels[] = {{2, 128, 256, 64, 0, &launch_w64<_Float16, false, 4>, 4, &w64_walk_blocks},
+                                      {2, 128, 256, 64, 1, &launch_w64<_Float16, true, 4>, 4, &w64_walk_blocks},
                                       {2, 128, 128, 64, 0, &launch_w64<_Float16, false, 2>, 2},
                                       {2, 128, 128, 64, 1, &launch_w64<_Float16, true, 2>, 2}};
 #endif

@@ -5,6 +5,7 @@
 // stream.  Holds no state except a thread-local error message.
 #include "fa.h"
 
+#include <algorithm>
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
@@ -145,8 +146,12 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
         return fail(FA_ERR_UNSUPPORTED, buf);
     }
     const uint64_t ntiles = ((uint64_t)N + e->block_m - 1) / e->block_m;
-    const uint64_t grid = (uint64_t)B * (uint64_t)Hq * ntiles;
+    uint64_t grid = (uint64_t)B * (uint64_t)Hq * ntiles;
     if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if (e->blocks) {
+        const long long walk = e->blocks((long long)B * Hq, (long long)ntiles, causal);
+        if (walk > 0) grid = (uint64_t)walk;
+    }
     if (stamps) {
         const uint64_t slots = grid * (uint64_t)(e->waves ? e->waves : e->block_m / 32);   // one per wave
         if (stamp_slots < 0 || (uint64_t)stamp_slots < slots)
@@ -175,6 +180,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
+    p.walk = 0;
     p.stamps = stamps;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
@@ -253,6 +259,7 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
     p.n_qtiles = (int)ntiles;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
     p.xcd_map = 0;
+    p.walk = 0;
     p.stamps = nullptr;
     const hipError_t err = e->launch(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
@@ -493,8 +500,18 @@ long long fa_fwd_stamp_slots(int B, int Hq, int N, int d, int dtype)
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return -1;
     const fa::KernelEntry* e = find_kernel(dtype, d, 0, 0, 0, (long long)B * Hq, N);
     if (!e) return -1;
-    return (long long)B * Hq * (((long long)N + e->block_m - 1) / e->block_m) *
-           (e->waves ? e->waves : e->block_m / 32);
+    const long long ntiles = ((long long)N + e->block_m - 1) / e->block_m;
+    long long grid = (long long)B * Hq * ntiles;
+    if (e->blocks) {
+        // the walk may differ with the mask: room for the larger launch
+        long long most = 0;
+        for (int causal = 0; causal < 2; ++causal) {
+            const long long walk = e->blocks((long long)B * Hq, ntiles, causal);
+            most = std::max(most, walk > 0 ? walk : grid);
+        }
+        grid = most;
+    }
+    return grid * (e->waves ? e->waves : e->block_m / 32);
 }
 
 int fa_wall_clock_khz(int device)

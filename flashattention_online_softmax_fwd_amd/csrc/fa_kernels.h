@@ -22,12 +22,16 @@ struct FwdParams {
     int n_qtiles;    // ceil(N / block_m)
     float scale_log2;  // scale * log2(e): scores go straight to the exp2 domain
     int xcd_map;       // 1: block order spreads whole heads over the 8 XCDs (set by the launcher)
+    int walk;          // 1: each workgroup walks pairs of query tiles (set by the launcher)
     // Square 16-bit forward only, else null: per wave {real-time start, real-time end,
     // shader-cycle start, shader-cycle end}, at [(block * waves + wave) * 4].
     unsigned long long* stamps;
 };
 
 using Launcher = hipError_t (*)(const FwdParams&, hipStream_t);
+// Workgroups of a launch that walks several query tiles per workgroup, or 0 for one
+// workgroup per query tile (units = B * Hq, ntiles = query tiles per head).
+using Blocks = long long (*)(long long units, long long ntiles, int causal);
 
 // One compiled instantiation.
 struct KernelEntry {
@@ -38,6 +42,7 @@ struct KernelEntry {
     int causal;
     Launcher launch;
     int waves;      // waves per workgroup; 0: block_m / 32 (one 32-row block per wave)
+    Blocks blocks;  // null: one workgroup per query tile
 };
 
 // Tables defined by the kernel translation units.

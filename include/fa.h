@@ -127,8 +127,11 @@ int fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* ls
  *                stamps[4w + 2], [4w + 3] = the shader-cycle counter at the same
  *                two points, so (cycles / real-time ticks) * wall clock rate is the
  *                wave's average shader clock.  Must not overlap any other argument.
- *   stamp_slots  the buffer's capacity in waves; fa_fwd_stamp_slots gives the
- *                number the launch has (fewer: FA_ERR_INVALID_ARG)
+ *   stamp_slots  the buffer's capacity in waves; fa_fwd_stamp_slots gives a
+ *                number the launch cannot exceed (fewer than the launch has:
+ *                FA_ERR_INVALID_ARG); slots past the launch's waves are not
+ *                written.  A wave may cover several query tiles in turn: its
+ *                stamps span all of them
  *   other arguments, ownership and errors: as for fa_fwd; FA_DTYPE_F32 returns
  *   FA_ERR_UNSUPPORTED.  o and lse are bitwise the same as fa_fwd's.
  */
