@@ -1,31 +1,37 @@
 // fa_fwd_w64.hip -- FlashAttention forward for gfx950 (CDNA4, MI355X), 16-bit inputs
-// (bf16 or fp16), head dimension 128: 64 query rows per wave, one wave per SIMD.
+// (bf16 or fp16), head dimension 64 or 128: 64 query rows per wave, one wave per SIMD.
 //
 // Same method and the same per-row arithmetic as fwd16_kernel (fa_fwd_mfma16.hip): the
 // online softmax of the pages in base 2 (mbrenndoerfer.com "Online Softmax Computation",
 // its update equations; spicyshark.co online-softmax lesson, "The idea", "From softmax to
 // attention" and "The implementation"), query blocks outer and key blocks inner (kbwen.com
-// FlashAttention feed, "More than two blocks"), with the reference m moved only when the
-// row maximum has grown by more than 2^8 (l and O share the stale reference, so u / l is
-// unchanged), and the guard for rows with no finite score yet (0 as the exp reference).
-// P is summed into l in fp32 before it is rounded to the element type for the PV product.
+// FlashAttention feed, "More than two blocks"), with a lazy reference m: it moves only when a
+// row maximum has outrun it by more than a slack (bf16: 2^48, fp16: 2^15, so that P stays
+// representable; l and O share the stale reference, so u / l is unchanged), and the guard
+// for rows with no finite score yet (0 as the exp reference).  P is summed into l in fp32
+// before it is rounded to the element type for the PV product.
 //
-// What differs is the shape of the work.  A workgroup of 2 waves owns 128 query rows; each
-// wave owns 64 of them as two 32-row blocks, so every K or V operand read from LDS feeds two
-// matrix products (half the LDS reads per flop of a 32-row wave).  Two workgroups share a
-// CU: one wave per SIMD.  The output accumulators (128 per lane) stay in AGPRs for the whole
-// key walk, so the register file holds Q, two score buffers and two weight buffers beside
-// them.  The key walk runs in 32-key halves of the 64-key LDS tiles; in half h a wave issues
-// the score products of half h+1 and the value products of half h-1 while its vector unit
-// runs the softmax of half h.  That schedule is written out as assembly by gen_fwd_kloop.py
-// (fa_fwd_kloop.inc): the compiler would copy the accumulators out of the AGPRs for the rare
-// rescale and would not keep the three streams interleaved.  This file computes the
-// addresses and hands them to that assembly; the assembly loads Q, walks the tiles and
-// stores O and LSE.
+// What differs is the shape of the work.  Each wave owns 64 query rows as two 32-row
+// blocks, so every K or V operand read from LDS feeds two matrix products (half the LDS
+// reads per flop of a 32-row wave), and runs alone on its SIMD.  A workgroup is 2 waves (128
+// rows; two workgroups per CU) or 4 waves (256 rows; one per CU, all four SIMDs), and the
+// waves split each tile's loads.  The output accumulators (128 per lane at d = 128) stay in
+// AGPRs for the whole key walk, so the register file holds Q, two score buffers and two
+// weight buffers beside them.  The key walk runs in 32-key halves of the 64-key LDS tiles;
+// in half h a wave issues the score products of half h+1 and the value products of half h-1
+// while its vector unit runs the softmax of half h.  That schedule is written out as
+// assembly by gen_fwd_kloop.py (fa_fwd_kloop.inc): the compiler would copy the accumulators
+// out of the AGPRs for the rare rescale and would not keep the three streams interleaved.
+// This file computes the addresses and hands them to that assembly; the assembly loads Q,
+// walks the tiles and stores O and LSE.
 //
-// LDS (64 KiB per workgroup): K tiles at +0 and +16 KiB, V tiles at +32 and +48 KiB, each
-// [64 keys][128 dims] with 16-byte chunks XOR-swizzled per row (the layout of
-// fa_fwd_mfma16.hip), filled by buffer_load_dwordx4 ... lds.  Rows past N read as zero and
+// 256-row workgroups walk pairs of query tiles (the heaviest causal tile of a head with its
+// lightest) when that balances as well as one tile per workgroup: one workgroup per CU,
+// no dispatch gaps, and every CU gets the same causal work.
+//
+// LDS (4 tiles: 64 KiB at d = 128, 32 KiB at d = 64): K tiles at +0 and +TILE, V tiles at
+// +2 TILE and +3 TILE, each [64 keys][d] with 16-byte chunks XOR-swizzled per row (the layout
+// of fa_fwd_mfma16.hip), filled by buffer_load_dwordx4 ... lds.  Rows past N read as zero and
 // rows of O and LSE past N are not written: every buffer range ends at the head's last row.
 #include "fa_kernels.h"
 #include "fa_mfma16_common.h"
@@ -67,17 +73,21 @@ namespace fa {
     "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156",  \
     "a157", "a158", "a159", "vcc", "m0", "scc", "memory"
 
-template <typename E, bool CAUSAL, int NW>
+template <typename E, bool CAUSAL, int NW, int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_w64_kernel(const FwdParams p)
 {
     static_assert(NW == 2 || NW == 4, "two or four waves of 64 rows");
-    constexpr int D = 128;
+    constexpr int R = 64;             // query rows per wave
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     constexpr int ROWB = D * 2;
-    constexpr int BM = 64 * NW;   // query rows of the workgroup
-    // K0, K1, V0, V1.  Aligned to 32 KiB: the walk switches buffers by flipping bit 14 of
-    // the addresses.
-    __shared__ __attribute__((aligned(32768))) char lds[65536];
+    constexpr int TILE = 64 * ROWB;   // one 64-key K or V tile
+    constexpr int BM = R * NW;        // query rows of the workgroup
+    constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+    constexpr int RPS = 1024 / ROWB;  // rows per 1 KiB load slice
+    // K0, K1, V0, V1 at 0, TILE, 2 TILE, 3 TILE.  Aligned to 32 KiB: the walk switches buffers
+    // by flipping the TILE bit of the addresses.
+    __shared__ __attribute__((aligned(32768))) char lds[4 * TILE];
 
     const int N = p.N;
     const int units = p.B * p.Hq;
@@ -142,7 +152,7 @@ fwd_w64_kernel(const FwdParams p)
     const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)Lh, (short)0, N * 4, 0x00020000);
 
     const int q0 = qt * BM;
-    const int row0 = q0 + 64 * wave;                    // the wave's first query row
+    const int row0 = q0 + R * wave;                     // the wave's first query row
     const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
     const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
     const int loff = (row0 + l32) * 4;
@@ -150,34 +160,34 @@ fwd_w64_kernel(const FwdParams p)
 
     // K operand: row l32 of the 32-key block, logical chunk 2kk + hi (buffer K0 to start).
     const int kx = swz<D>(l32);
-    int koff[8];
+    int koff[8] = {};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) koff[kk] = (int)ldsb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
+    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)ldsb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
     // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
     // step and dims 32dt + 16(G&1) + 4s ..; buffer V1 to start (the walk flips to V0 first).
     const int G = lane >> 4;
     const int jj = (lane >> 2) & 3;
     const int ss = lane & 3;
-    int voff[8];
+    int voff[8] = {};
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int row = 8 * r + 4 * (G >> 1) + jj;
         const int w = swz<D>(row);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < D / 32; ++dt) {
             const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
-            voff[4 * r + dt] = (int)ldsb + 49152 + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+            voff[(D / 32) * r + dt] = (int)ldsb + 3 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
         }
     }
     // Tile loads: slice ii = wave + NW i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
-    // lane's 16 bytes are row 4ii + lane/16, physical chunk lane%16, i.e. logical chunk
-    // (lane%16) ^ swz(row).  Only ii's low two bits enter the swizzle: two patterns (i even, odd;
-    // the same pattern when NW = 4).
+    // lane's 16 bytes are row RPS ii + lane / CPR, physical chunk lane % CPR, i.e. logical chunk
+    // (lane % CPR) ^ swz(row).  ii enters the swizzle only through ii mod 4 (d = 128) or ii mod 2
+    // (d = 64): two patterns (i even, odd; the same one when NW = 4).
     int dma[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int row = 4 * (wave + NW * e) + (lane >> 4);
-        dma[e] = 1024 * wave + (lane >> 4) * ROWB + 16 * ((lane & 15) ^ swz<D>(row));
+        const int row = RPS * (wave + NW * e) + lane / CPR;
+        dma[e] = 1024 * wave + (lane / CPR) * ROWB + 16 * ((lane % CPR) ^ swz<D>(row));
     }
     const int dmask = l32 - 4 * hi;   // causal: key 8(r>>2) + (r&3) + 4hi of a diagonal half visible iff <= row l32
     const int hi4 = 4 * hi;
@@ -185,7 +195,7 @@ fwd_w64_kernel(const FwdParams p)
     // Key tiles of 64 for the workgroup; the last one this wave's rows need.
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int nt = (kv_end + 63) / 64;
-    const int last = CAUSAL ? min(nt - 1, q0 / 64 + wave) : nt - 1;
+    const int last = CAUSAL ? min(nt - 1, (q0 + R * wave) / 64) : nt - 1;
     const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
     const int limA = valid_last - 1;
     const int limB = valid_last - 33;
@@ -193,11 +203,11 @@ fwd_w64_kernel(const FwdParams p)
     const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
 
-    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 32768 + 1024 * wave;
+    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 2 * TILE + 1024 * wave;
     unsigned soff, kit, cnt;
     unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
     int dlim;
-#define FA_W64_ASM(TEXT)                                                                                   \
+#define FA_W64_ASM_C(TEXT, CLOBBERS)                                                                       \
     asm volatile(TEXT                                                                                      \
                  : [koff0] "+v"(koff[0]), [koff1] "+v"(koff[1]), [koff2] "+v"(koff[2]), [koff3] "+v"(koff[3]),  \
                    [koff4] "+v"(koff[4]), [koff5] "+v"(koff[5]), [koff6] "+v"(koff[6]), [koff7] "+v"(koff[7]),  \
@@ -212,25 +222,32 @@ fwd_w64_kernel(const FwdParams p)
                    [dmask] "v"(dmask), [hi4] "v"(hi4), [krs] "s"(krs), [vrs] "s"(vrs), [qrs] "s"(qrs),             \
                    [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
                    [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip)                                                 \
-                 : FA_W64_CLOBBERS)
-    if constexpr (NW == 2) {
-        if constexpr (__is_same(E, __bf16)) {
-            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W2);
-            else FA_W64_ASM(FA_KLOOP_BF16_FULL_W2);
+                 : CLOBBERS)
+#define FA_W64_ASM(TEXT) FA_W64_ASM_C(TEXT, FA_W64_CLOBBERS)
+#define FA_W64_PICK(W, DD)                                                                 \
+    if constexpr (__is_same(E, __bf16)) {                                                 \
+        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W##W##_D##DD);              \
+        else FA_W64_ASM(FA_KLOOP_BF16_FULL_W##W##_D##DD);                                 \
+    } else {                                                                              \
+        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W##W##_D##DD);               \
+        else FA_W64_ASM(FA_KLOOP_F16_FULL_W##W##_D##DD);                                  \
+    }
+    if constexpr (D == 128) {
+        if constexpr (NW == 2) {
+            FA_W64_PICK(2, 128)
         } else {
-            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W2);
-            else FA_W64_ASM(FA_KLOOP_F16_FULL_W2);
+            FA_W64_PICK(4, 128)
         }
     } else {
-        if constexpr (__is_same(E, __bf16)) {
-            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W4);
-            else FA_W64_ASM(FA_KLOOP_BF16_FULL_W4);
+        if constexpr (NW == 2) {
+            FA_W64_PICK(2, 64)
         } else {
-            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W4);
-            else FA_W64_ASM(FA_KLOOP_F16_FULL_W4);
+            FA_W64_PICK(4, 64)
         }
     }
+#undef FA_W64_PICK
 #undef FA_W64_ASM
+#undef FA_W64_ASM_C
     // every wave is done with the LDS tiles before the next item loads its own
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
@@ -243,13 +260,15 @@ fwd_w64_kernel(const FwdParams p)
     }
 }
 
-#define FA_W64_INSTANTIATE(NW)                                                  \
-    template __global__ void fwd_w64_kernel<__bf16, false, NW>(const FwdParams);   \
-    template __global__ void fwd_w64_kernel<__bf16, true, NW>(const FwdParams);    \
-    template __global__ void fwd_w64_kernel<_Float16, false, NW>(const FwdParams); \
-    template __global__ void fwd_w64_kernel<_Float16, true, NW>(const FwdParams);
-FA_W64_INSTANTIATE(2)
-FA_W64_INSTANTIATE(4)
+#define FA_W64_INSTANTIATE(NW, DD)                                                      \
+    template __global__ void fwd_w64_kernel<__bf16, false, NW, DD>(const FwdParams);   \
+    template __global__ void fwd_w64_kernel<__bf16, true, NW, DD>(const FwdParams);    \
+    template __global__ void fwd_w64_kernel<_Float16, false, NW, DD>(const FwdParams); \
+    template __global__ void fwd_w64_kernel<_Float16, true, NW, DD>(const FwdParams);
+FA_W64_INSTANTIATE(2, 128)
+FA_W64_INSTANTIATE(4, 128)
+FA_W64_INSTANTIATE(2, 64)
+FA_W64_INSTANTIATE(4, 64)
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 namespace {
@@ -295,7 +314,7 @@ long long w64_walk_blocks(long long units, long long ntiles, int causal)
     return g;
 }
 
-template <typename E, bool CAUSAL, int NW>
+template <typename E, bool CAUSAL, int NW, int D>
 hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
 {
     const long long units = (long long)p.B * p.Hq;
@@ -311,7 +330,7 @@ hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
         args.xcd_map = (units % 8 == 0) ? 1 : 0;   // needs whole heads per XCD
     }
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL, NW>, dim3((unsigned)grid), dim3(64 * NW),
+    return hipLaunchKernel((const void*)&fwd_w64_kernel<E, CAUSAL, NW, D>, dim3((unsigned)grid), dim3(64 * NW),
                            kargs, 0, stream);
 }
 
@@ -320,14 +339,14 @@ hipError_t launch_w64(const FwdParams& p, hipStream_t stream)
 // 256-row workgroups first: one K/V tile load per CU instead of two (2-3% faster on the causal
 // d = 128 workloads); the host falls back to 128-row workgroups for grids too small to give
 // every CU two of them.
-const KernelEntry kBf16W64Kernels[] = {{1, 128, 256, 64, 0, &launch_w64<__bf16, false, 4>, 4, &w64_walk_blocks},
-                                       {1, 128, 256, 64, 1, &launch_w64<__bf16, true, 4>, 4, &w64_walk_blocks},
-                                       {1, 128, 128, 64, 0, &launch_w64<__bf16, false, 2>, 2},
-                                       {1, 128, 128, 64, 1, &launch_w64<__bf16, true, 2>, 2}};
-const KernelEntry kF16W64Kernels[] = {{2, 128, 256, 64, 0, &launch_w64<_Float16, false, 4>, 4, &w64_walk_blocks},
-                                      {2, 128, 256, 64, 1, &launch_w64<_Float16, true, 4>, 4, &w64_walk_blocks},
-                                      {2, 128, 128, 64, 0, &launch_w64<_Float16, false, 2>, 2},
-                                      {2, 128, 128, 64, 1, &launch_w64<_Float16, true, 2>, 2}};
+#define FA_W64_ENTRIES(CODE, E, DD)                                                             \
+    {CODE, DD, 256, 64, 0, &launch_w64<E, false, 4, DD>, 4, &w64_walk_blocks},                  \
+        {CODE, DD, 256, 64, 1, &launch_w64<E, true, 4, DD>, 4, &w64_walk_blocks},               \
+        {CODE, DD, 128, 64, 0, &launch_w64<E, false, 2, DD>, 2, nullptr},                       \
+        {CODE, DD, 128, 64, 1, &launch_w64<E, true, 2, DD>, 2, nullptr}
+const KernelEntry kBf16W64Kernels[] = {FA_W64_ENTRIES(1, __bf16, 128), FA_W64_ENTRIES(1, __bf16, 64)};
+const KernelEntry kF16W64Kernels[] = {FA_W64_ENTRIES(2, _Float16, 128), FA_W64_ENTRIES(2, _Float16, 64)};
+#undef FA_W64_ENTRIES
 #endif
 
 }  // namespace fa

@@ -52,8 +52,8 @@ const fa::KernelEntry* table_for(int dtype, int* n)
 const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n, long long units = 0,
                                    long long N = 0)
 {
-    // 16-bit inputs at d = 128: the 64-rows-per-wave kernels serve the 256 x 64 and 128 x 64 tiles
-    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128) {
+    // 16-bit inputs: the 64-rows-per-wave kernels serve the 256 x 64 and 128 x 64 tiles
+    if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) {
         const fa::KernelEntry* w = dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels;
         if (block_m == 0 && block_n == 0) {
             // 256-row workgroups when the grid gives every CU at least two of them, else 128-row
@@ -63,7 +63,8 @@ const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, in
             block_n = 64;
         }
         for (int i = 0; i < fa::kNumW64Kernels; ++i)
-            if (w[i].causal == causal && w[i].block_m == block_m && w[i].block_n == block_n) return &w[i];
+            if (w[i].d == d && w[i].causal == causal && w[i].block_m == block_m && w[i].block_n == block_n)
+                return &w[i];
     }
     int n = 0;
     const fa::KernelEntry* table = table_for(dtype, &n);
@@ -584,7 +585,7 @@ int fa_tile_shapes(int dtype, int d, int* block_m, int* block_n, int cap)
             ++count;
         }
     };
-    if ((dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128)
+    if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16)
         add(dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels, fa::kNumW64Kernels);
     int n = 0;
     const fa::KernelEntry* table = table_for(dtype, &n);

@@ -56,7 +56,7 @@ extern const int kNumF32Kernels;
 // 256 x 64 tiles (4 waves); the default for 16-bit inputs at d = 128 comes first.
 extern const KernelEntry kBf16W64Kernels[];
 extern const KernelEntry kF16W64Kernels[];
-constexpr int kNumW64Kernels = 4;
+constexpr int kNumW64Kernels = 8;
 // Split-KV partial-state kernels (16-bit inputs, float partial outputs).
 extern const KernelEntry kBf16SplitKernels[];
 extern const int kNumBf16SplitKernels;

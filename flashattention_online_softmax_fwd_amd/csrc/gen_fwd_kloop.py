@@ -45,6 +45,29 @@ OUT = os.environ.get("OUT_INC") or os.path.join(HERE, "fa_fwd_kloop.inc")
 
 NEG_INF_BITS = "0xff800000"
 
+# Head dimension of the variant being assembled (64 or 128); set by assemble().
+D = 128
+
+
+def KK():
+    """16-dim steps of the score products (Q operand registers per row block / 4)."""
+    return D // 16
+
+
+def DB():
+    """32-dim column blocks of O."""
+    return D // 32
+
+
+def ROWB():
+    """Bytes of one K, V, Q or O row."""
+    return 2 * D
+
+
+def TILE():
+    """Bytes of one 64-key K or V tile in LDS (buffers at 0, TILE, 2 TILE, 3 TILE)."""
+    return 64 * ROWB()
+
 # ---------------------------------------------------------------- registers
 
 def vr(i):
@@ -55,46 +78,49 @@ def vrange(a, n):
     return "v[%d:%d]" % (a, a + n - 1)
 
 
-def Qr(rb, kk):
-    return 32 * rb + 4 * kk
-
-
-def Sr(buf, rb):
-    return 64 + 32 * buf + 16 * rb
-
-
-def Pr(buf, rb, ks):
-    return 128 + 16 * buf + 8 * rb + 4 * ks
-
-
-def KST(i):
-    return 160 + 4 * i
-
-
-def VST(i):
-    return 176 + 4 * i
-
-
-def Mr(rb):
-    return 192 + rb
-
-
-def Lr(rb):
-    return 194 + rb
-
-
-def ALr(par, rb):
-    return 196 + 2 * par + rb
-
-
+# Register plan (see the module docstring).
+PLAN = dict(Q0=0, S0=64, P0=128, KST0=160, VST0=176, M0=192)
 TMP0 = 200           # v200..v223
 NTMP = 24
 NEGINF = 223         # holds -inf for lane-mask selects
 NVCLOB = 224         # v0..v223 clobbered
 
 
+def Qr(rb, kk):
+    return PLAN["Q0"] + 4 * KK() * rb + 4 * kk
+
+
+def Sr(buf, rb):
+    return PLAN["S0"] + 32 * buf + 16 * rb
+
+
+def Pr(buf, rb, ks):
+    return PLAN["P0"] + 16 * buf + 8 * rb + 4 * ks
+
+
+def KST(i):
+    return PLAN["KST0"] + 4 * i
+
+
+def VST(i):
+    return PLAN["VST0"] + 4 * i
+
+
+def Mr(rb):
+    return PLAN["M0"] + rb
+
+
+def Lr(rb):
+    return PLAN["M0"] + 2 + rb
+
+
+def ALr(par, rb):
+    return PLAN["M0"] + 4 + 2 * par + rb
+
+
 def Or(rb, db):
-    return 64 * rb + 16 * db
+    """First AGPR of O's 32 x 32 block db of row block rb."""
+    return 16 * DB() * rb + 16 * db
 
 
 # Row sums: "valu" adds the fp32 P with vector adds (the default); "mfma16" adds the rounded
@@ -102,9 +128,12 @@ def Or(rb, db):
 # lane's four results the sum over both lane halves of the lane's own row (see ones16), so l
 # sits in AGPRs beside O.  Measured equal on the causal d = 128 workloads (64 vector adds per
 # tile traded for 8 small products); an all-ones 32x32x16 product instead was 2-5% slower.
-ROWSUM = os.environ.get("FA_GEN_ROWSUM", "valu")
-if ROWSUM not in ("valu", "mfma16"):
-    raise SystemExit("FA_GEN_ROWSUM must be valu or mfma16")
+# Per head dimension (FA_GEN_ROWSUM for d = 128, FA_GEN_ROWSUM64 for d = 64).
+ROWSUM_BY_D = {128: os.environ.get("FA_GEN_ROWSUM", "valu"), 64: os.environ.get("FA_GEN_ROWSUM64", "valu")}
+for _r in ROWSUM_BY_D.values():
+    if _r not in ("valu", "mfma16"):
+        raise SystemExit("FA_GEN_ROWSUM and FA_GEN_ROWSUM64 must be valu or mfma16")
+ROWSUM = ROWSUM_BY_D[128]
 ONES = 216           # v216..v219: the 0/1 A operand of the row-sum products
 MFMA_ROWSUM = ROWSUM == "mfma16"
 LACC_REGS = 4
@@ -335,15 +364,15 @@ class Gen:
     # ---- operand reads from LDS
     def k_read(self, i, kk, t):
         """K operand for dims 16kk.. of keys 32t.. of the current K tile into staging i."""
-        return Ins("ds_read_b128 %s, %%[koff%d] offset:%d" % (vrange(KST(i), 4), kk, 8192 * t), "lds",
+        return Ins("ds_read_b128 %s, %%[koff%d] offset:%d" % (vrange(KST(i), 4), kk, 32 * ROWB() * t), "lds",
                    defs=regs(KST(i), 4))
 
     def v_reads(self, i, db, ks, t):
         """V^T operand of dims 32db.. and keys 32t + 16ks.. (two transposing reads)."""
-        off = 8192 * t + 4096 * ks
+        off = 32 * ROWB() * t + 16 * ROWB() * ks
         return [Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i), 2), db, off), "lds",
                     defs=regs(VST(i), 2)),
-                Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i) + 2, 2), 4 + db, off), "lds",
+                Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i) + 2, 2), DB() + db, off), "lds",
                     defs=regs(VST(i) + 2, 2))]
 
     def mfma_s(self, sbuf, rb, kk, st):
@@ -366,7 +395,7 @@ class Gen:
         """S(h+1) into S buffer sbuf from K tile rows 32t..: per kk one K read feeding the
         products of every active row block."""
         out = []
-        for kk in range(8):
+        for kk in range(KK()):
             st = kk % 4
             prods = [self.mfma_s(sbuf, rb, kk, st) for rb in rbs]
             out.append(([self.k_read(st, kk, t)], prods))
@@ -385,7 +414,7 @@ class Gen:
         out = []
         n = 0
         for ks in range(2):
-            for db in range(4):
+            for db in range(DB()):
                 st = n % 4
                 n += 1
                 prods = [self.mfma_pv(pbuf, rb, db, ks, st) for rb in rbs]
@@ -535,7 +564,7 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
 def rescale_block(par, rbs):
     """O *= alpha[par] on the row blocks rbs: read, multiply, write back, 8 at a time."""
     out = [Ins("s_nop 7", "nop")]
-    regs_list = [(rb, Or(rb, db) + r) for rb in rbs for db in range(4) for r in range(16)]
+    regs_list = [(rb, Or(rb, db) + r) for rb in rbs for db in range(DB()) for r in range(16)]
     if MFMA_ROWSUM:
         regs_list += [(rb, Lacc(rb) + r) for rb in rbs for r in range(LACC_REGS)]
     for i in range(0, len(regs_list), 8):
@@ -596,13 +625,14 @@ def merge_half(prod_streams, valu, extra, lead=2, preissued=0, head_valu=0, next
 # ---------------------------------------------------------------- tile loads (LDS DMA)
 
 def dma_tile(which, nw):
-    """This wave's share of one 64-key K or V tile (16 slices of 1 KiB, slice ii = wave + nw*i)
+    """This wave's share of one 64-key K or V tile (TILE / 1 KiB slices, slice ii = wave + nw*i)
     from %[<which>src] (byte offset of the tile in the head) into the buffer at %[<which>dst]
     (LDS address of this wave's first slice in the tile's buffer).  The lane's source offset
-    within a slice depends on ii only through ii mod 4: %[dma0] (i even) and %[dma1] (i odd)."""
+    within a slice depends on ii only through ii mod 4 (d = 128) or ii mod 2 (d = 64):
+    %[dma0] (i even) and %[dma1] (i odd)."""
     out = []
     rs = "%[krs]" if which == "k" else "%[vrs]"
-    for i in range(16 // nw):
+    for i in range(TILE() // 1024 // nw):
         out.append(Ins("s_add_u32 m0, %%[%sdst], %d" % (which, 1024 * nw * i), "m0", defs=["m0"]))
         out.append(Ins("s_add_u32 %%[soff], %%[%ssrc], %d" % (which, 1024 * nw * i), "salu", defs=["%[soff]"]))
         out.append(Ins("buffer_load_dwordx4 %%[dma%d], %s, %%[soff] offen lds" % (i & 1, rs), "dma",
@@ -611,24 +641,24 @@ def dma_tile(which, nw):
 
 
 def advance_k():
-    """Next K tile: source +16 KiB, LDS buffer toggled."""
-    return [Ins("s_add_u32 %[ksrc], %[ksrc], 16384", "salu", defs=["%[ksrc]"], uses=["%[ksrc]"]),
-            Ins("s_xor_b32 %[kdst], %[kdst], 16384", "salu", defs=["%[kdst]"], uses=["%[kdst]"])]
+    """Next K tile: source + one tile, LDS buffer toggled."""
+    return [Ins("s_add_u32 %%[ksrc], %%[ksrc], %d" % TILE(), "salu", defs=["%[ksrc]"], uses=["%[ksrc]"]),
+            Ins("s_xor_b32 %%[kdst], %%[kdst], %d" % TILE(), "salu", defs=["%[kdst]"], uses=["%[kdst]"])]
 
 
 def advance_v():
-    return [Ins("s_add_u32 %[vsrc], %[vsrc], 16384", "salu", defs=["%[vsrc]"], uses=["%[vsrc]"]),
-            Ins("s_xor_b32 %[vdst], %[vdst], 16384", "salu", defs=["%[vdst]"], uses=["%[vdst]"])]
+    return [Ins("s_add_u32 %%[vsrc], %%[vsrc], %d" % TILE(), "salu", defs=["%[vsrc]"], uses=["%[vsrc]"]),
+            Ins("s_xor_b32 %%[vdst], %%[vdst], %d" % TILE(), "salu", defs=["%[vdst]"], uses=["%[vdst]"])]
 
 
 def toggle_reads():
     """Switch the K and V operand reads to the other buffer of each."""
     out = []
-    for kk in range(8):
-        out.append(Ins("v_xor_b32_e32 %%[koff%d], 0x4000, %%[koff%d]" % (kk, kk), "valu",
+    for kk in range(KK()):
+        out.append(Ins("v_xor_b32_e32 %%[koff%d], 0x%x, %%[koff%d]" % (kk, TILE(), kk), "valu",
                        defs=["%%[koff%d]" % kk], uses=["%%[koff%d]" % kk]))
-    for i in range(8):
-        out.append(Ins("v_xor_b32_e32 %%[voff%d], 0x4000, %%[voff%d]" % (i, i), "valu",
+    for i in range(2 * DB()):
+        out.append(Ins("v_xor_b32_e32 %%[voff%d], 0x%x, %%[voff%d]" % (i, TILE(), i), "valu",
                        defs=["%%[voff%d]" % i], uses=["%%[voff%d]" % i]))
     return out
 
@@ -696,18 +726,21 @@ def build(elem, causal, nw):
         prog.append(Ins("v_mov_b32 %s, %s" % (vr(Mr(rb)), NEG_INF_BITS), "valu", defs=[vr(Mr(rb))]))
         prog.append(Ins("v_mov_b32 %s, 0" % vr(Lr(rb)), "valu", defs=[vr(Lr(rb))]))
     prog.append(Ins("s_mov_b32 %[kit], 1", "salu", defs=["%[kit]"]))
-    prog.append(Ins("v_add_u32_e32 %s, 0x2000, %%[qoff]" % vr(t(0)), "valu", defs=[vr(t(0))]))
+    prog.append(Ins("v_add_u32_e32 %s, 0x%x, %%[qoff]" % (vr(t(0)), 32 * ROWB()), "valu", defs=[vr(t(0))]))
     for rb in all_rb:
-        for kk in range(8):
+        for kk in range(KK()):
             base = "%[qoff]" if rb == 0 else vr(t(0))
             prog.append(Ins("buffer_load_dwordx4 %s, %s, %%[qrs], 0 offen offset:%d" % (vrange(Qr(rb, kk), 4), base, 32 * kk),
                             "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else [vr(t(0))]))
-    for a in range(128 + 2 * LACC_REGS if MFMA_ROWSUM else 128):
+    zero = list(range(32 * DB()))
+    if MFMA_ROWSUM:
+        zero += list(range(Lacc(0), Lacc(0) + 2 * LACC_REGS))
+    for a in zero:
         prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
     if MFMA_ROWSUM:
         prog.extend(ones16(elem))
     prog.append(Ins("s_waitcnt vmcnt(0)", "wait"))
-    for r in range(64):
+    for r in range(8 * KK()):
         prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
     # ---- first tiles: K(0), K(1) (if any), V(0)
     prog.extend(dma_tile("k", nw))
@@ -849,15 +882,17 @@ def epilogue(g):
         out.append(Ins("buffer_store_dword %s, %s, %%[lrs], 0 offen" % (lg, loff), "vstore", uses=[lg, loff]))
         ooff = "%[ooff]" if rb == 0 else vr(t(18))
         if rb == 1:
-            out.append(Ins("v_add_u32_e32 %s, 0x2000, %%[ooff]" % vr(t(18)), "valu", defs=[vr(t(18))]))
-        for db in range(4):
+            out.append(Ins("v_add_u32_e32 %s, 0x%x, %%[ooff]" % (vr(t(18)), 32 * ROWB()), "valu", defs=[vr(t(18))]))
+        for db in range(DB()):
             for gq in range(4):
                 a0 = Or(rb, db) + 4 * gq
                 tv = [vr(t(j)) for j in range(4)]
                 for j in range(4):
-                    out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (tv[j], a0 + j), "accr", defs=[tv[j]], uses=["a%d" % (a0 + j)]))
+                    out.append(Ins("v_accvgpr_read_b32 %s, a%d" % (tv[j], a0 + j), "accr", defs=[tv[j]],
+                                   uses=["a%d" % (a0 + j)]))
                 for j in range(4):
-                    out.append(Ins("v_mul_f32_e32 %s, %s, %s" % (tv[j], inv, tv[j]), "valu", defs=[tv[j]], uses=[tv[j], inv]))
+                    out.append(Ins("v_mul_f32_e32 %s, %s, %s" % (tv[j], inv, tv[j]), "valu", defs=[tv[j]],
+                                   uses=[tv[j], inv]))
                 pk = vr(t(8 + 2 * gq))
                 pk2 = vr(t(9 + 2 * gq))
                 out.append(Ins("%s %s, %s, %s" % (g.cvt_op, pk, tv[0], tv[1]), "valu", defs=[pk], uses=tv[:2]))
@@ -869,7 +904,11 @@ def epilogue(g):
     return out
 
 
-def assemble(elem, causal, nw):
+def assemble(elem, causal, nw, d=128):
+    global D, ROWSUM, MFMA_ROWSUM
+    D = d
+    ROWSUM = ROWSUM_BY_D[d]
+    MFMA_ROWSUM = ROWSUM == "mfma16"
     g, prog, pathA, pathB, tail = build(elem, causal, nw)
     st = State()
     out = []
@@ -896,12 +935,13 @@ def main():
              "// forward (fa_fwd_w64.hip) as gfx950 assembly, one string per element type, mask and\n"
              "// number of waves per workgroup (which share each tile's loads).\n"
              "#pragma once\n"]
-    for nw in (2, 4):
-        for elem in ("bf16", "f16"):
-            for causal in (False, True):
-                lines = assemble(elem, causal, nw)
-                name = "FA_KLOOP_%s_%s_W%d" % (elem.upper(), "CAUSAL" if causal else "FULL", nw)
-                parts.append("#define %s \\\n%s\n" % (name, " \\\n".join('    "%s\\n"' % l for l in lines)))
+    for d in (128, 64):
+        for nw in (2, 4):
+            for elem in ("bf16", "f16"):
+                for causal in (False, True):
+                    lines = assemble(elem, causal, nw, d)
+                    name = "FA_KLOOP_%s_%s_W%d_D%d" % (elem.upper(), "CAUSAL" if causal else "FULL", nw, d)
+                    parts.append("#define %s \\\n%s\n" % (name, " \\\n".join('    "%s\\n"' % l for l in lines)))
     text = "\n".join(parts)
     with open(OUT, "w") as f:
         f.write(text)
