@@ -81,17 +81,15 @@ def kernel_hash(source: str) -> str:
 
 def forward_kernel(w):
     """(KERNEL_SOURCES key, kernel name) of the forward the library dispatches for ``w`` by
-    default: fp32 has its own kernel; 16-bit inputs at d = 128 run the 64-rows-per-wave
-    kernel, in 256-row workgroups (4 waves) when the grid holds at least 512 of them and in
-    128-row workgroups (2 waves) otherwise; 16-bit inputs at d = 64 run fwd16_kernel."""
+    default: fp32 has its own kernel; 16-bit inputs run the 64-rows-per-wave kernel, in
+    256-row workgroups (4 waves) when the grid holds at least 512 of them and in 128-row
+    workgroups (2 waves) otherwise."""
     if w.dtype == "f32":
         return "f32", "fa::fwd_f32_kernel"
-    if w.d == 128:
-        units = w.B * w.Hq
-        nw = 4 if units * ((w.N + 255) // 256) >= 512 else 2
-        return "w64", "fa::fwd_w64_kernel<%s, %s, %d>" % (
-            "__bf16" if w.dtype == "bf16" else "_Float16", "true" if w.causal else "false", nw)
-    return w.dtype, "fa::fwd16_kernel<%s>" % w.dtype
+    units = w.B * w.Hq
+    nw = 4 if units * ((w.N + 255) // 256) >= 512 else 2
+    return "w64", "fa::fwd_w64_kernel<%s, %s, %d, %d>" % (
+        "__bf16" if w.dtype == "bf16" else "_Float16", "true" if w.causal else "false", nw, w.d)
 
 
 def traffic_for(workload: str, source: str):
@@ -187,8 +185,8 @@ def stamped_clock(w, q, k, v, o, lse):
         "sclk_ghz": float(cyc.sum()) / float(real.sum()) * khz * 1e3 / 1e9,
         "kernel_span_ms": span_ticks / khz,
         "waves": int(len(st)),
-        # share of SIMD time the waves held: the d = 128 kernels run one wave per SIMD
-        "simd_busy": float(real.sum()) / float(span_ticks * simds) if simds and w.d == 128 else None,
+        # share of SIMD time the waves held: the 16-bit kernels run one wave per SIMD
+        "simd_busy": float(real.sum()) / float(span_ticks * simds) if simds else None,
         "wave_ms_mean": float(real.mean()) / khz,
         "wave_ms_max": float(real.max()) / khz,
         "wall_clock_khz": khz,

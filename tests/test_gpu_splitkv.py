@@ -119,16 +119,24 @@ def test_split_and_merge_match_the_full_oracle(fa, oracle, case, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_one_range_equals_the_forward_bitwise(fa, d, causal, dtype):
-    """S = 1 over a square problem: the same state, normalised once, then merged with weight 1."""
+def test_one_range_matches_the_forward(fa, oracle, d, causal, dtype):
+    """S = 1 over a square problem: one range, normalised once and merged with weight 1, is the
+    whole attention.  The split kernel and the square forward are different kernels (the
+    square forward lets its reference lag further and sums in another order), so each meets
+    the bar against the oracle and they agree to within the sum of their bars."""
     q, k, v = fin.make_qkv(2, 4, 2, 333, d, dtype, 4000 + d)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     print("split S=1 vs forward d=%d causal=%d" % (d, causal), flush=True)
     o_ref, l_ref = fa.forward(qd, kd, vd, causal=causal)
     o, lse = fa.attention_kv(qd, kd, vd, causal=causal, num_splits=1)
     torch.cuda.synchronize()
-    assert torch.equal(o, o_ref)
-    assert torch.equal(lse, l_ref)
+    ro, rl = oracle.attention(q, k, v, causal=causal, scale=1.0 / math.sqrt(d))
+    atol, rtol = TOL[dtype]
+    check(o.float().cpu().numpy(), ro, atol, rtol, "split S=1 o")
+    check(lse.cpu().numpy(), rl, atol, rtol, "split S=1 lse")
+    check(o_ref.float().cpu().numpy(), ro, atol, rtol, "forward o")
+    check(o.float().cpu().numpy(), o_ref.float().cpu().numpy(), 2 * atol, 2 * rtol, "split S=1 o vs forward o")
+    check(lse.cpu().numpy(), l_ref.cpu().numpy(), 2 * atol, 2 * rtol, "split S=1 lse vs forward lse")
 
 
 @pytest.mark.parametrize("d", [64, 128])
