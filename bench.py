@@ -79,17 +79,26 @@ def kernel_hash(source: str) -> str:
     return hashlib.sha256(data + b"\0" + flags).hexdigest()
 
 
-def forward_kernel(w):
+def forward_kernel(w, simds=1024):
     """(KERNEL_SOURCES key, kernel name) of the forward the library dispatches for ``w`` by
-    default: fp32 has its own kernel; 16-bit inputs run the 64-rows-per-wave kernel, in
-    256-row workgroups (4 waves) when the grid holds at least 512 of them and in 128-row
-    workgroups (2 waves) otherwise."""
+    default: fp32 has its own kernel; 16-bit inputs run the 64-rows-per-wave kernel when its
+    waves cover every SIMD (``simds`` of the device), in 256-row workgroups (4 waves) when the
+    grid holds at least 512 of them and in 128-row workgroups (2 waves) otherwise, and the
+    32-rows-per-wave kernel (fwd16_kernel, 128-row workgroups) for fewer rows."""
     if w.dtype == "f32":
         return "f32", "fa::fwd_f32_kernel"
     units = w.B * w.Hq
+    tname = "__bf16" if w.dtype == "bf16" else "_Float16"
+    if units * ((w.N + 63) // 64) < simds:
+        return w.dtype, "fa::fwd16_kernel<%s, %d, 128, 64, %s, false>" % (tname, w.d, "true" if w.causal else "false")
     nw = 4 if units * ((w.N + 255) // 256) >= 512 else 2
-    return "w64", "fa::fwd_w64_kernel<%s, %s, %d, %d>" % (
-        "__bf16" if w.dtype == "bf16" else "_Float16", "true" if w.causal else "false", nw, w.d)
+    return "w64", "fa::fwd_w64_kernel<%s, %s, %d, %d>" % (tname, "true" if w.causal else "false", nw, w.d)
+
+
+def device_simds():
+    import torch
+
+    return 4 * torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def traffic_for(workload: str, source: str):
@@ -285,14 +294,16 @@ def run_workload(name, steps, warmup, with_cpu, cpu_budget, precondition_s=0.0):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     torch.cuda.synchronize()
+    src, kname = forward_kernel(w, device_simds())
     wall, per_ms, o, lse, pre = time_gpu(fa, qd, kd, vd, w, steps, warmup, precondition_s)
     clock = stamped_clock(w, qd, kd, vd, o, lse)
+    if clock and src != "w64":
+        clock["simd_busy"] = None        # the 32-rows-per-wave kernel runs two waves per SIMD
     ms_step = wall * 1e3 / steps
     tflops = w.flops * steps / wall / 1e12
     avg_launch_ms = sum(per_ms) / len(per_ms)
     achieved = w.flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    src, kname = forward_kernel(w)
     rec = {
         "metric": metric_for(w),
         "value": tflops,

@@ -273,20 +273,6 @@ FA_W64_INSTANTIATE(4, 64)
 #if !defined(__HIP_DEVICE_COMPILE__)
 namespace {
 
-// Compute units of the current device (cached per device).
-int device_cus()
-{
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 // 256-row workgroups walk pairs of query tiles: one workgroup per CU at most (each holds a
 // whole CU: one wave per SIMD), as many as give every workgroup the same number of pairs, a
 // multiple of 8 (whole groups of the XCD map).  0 (one tile per workgroup) when the tiles fit

@@ -47,21 +47,50 @@ const fa::KernelEntry* table_for(int dtype, int* n)
     }
 }
 
+}  // namespace
+
+namespace fa {
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+}  // namespace fa
+
+namespace {
+
 // units: B * Hq (query heads of the batch), N: query rows per head; they size the grid when the
 // default tile depends on it.
 const fa::KernelEntry* find_kernel(int dtype, int d, int causal, int block_m, int block_n, long long units = 0,
                                    long long N = 0)
 {
     // 16-bit inputs: the 64-rows-per-wave kernels serve the 256 x 64 and 128 x 64 tiles
-    if (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) {
-        const fa::KernelEntry* w = dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels;
-        if (block_m == 0 && block_n == 0) {
-            // 256-row workgroups when the grid gives every CU at least two of them, else 128-row
-            // ones (twice the workgroups for small grids)
+    bool w64 = dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
+    if (w64 && block_m == 0 && block_n == 0) {
+        // by default, only when its 64-row waves cover every SIMD (one wave per SIMD each);
+        // fewer rows go to the 32-rows-per-wave kernel of the table below, which runs twice the
+        // waves, two per SIMD
+        const int cus = fa::device_cus();
+        const uint64_t simds = 4 * (uint64_t)(cus > 0 ? cus : 256);
+        if ((uint64_t)units * (((uint64_t)N + 63) / 64) < simds) {
+            w64 = false;
+        } else {
+            // 256-row workgroups when the grid gives every CU at least two of them, else
+            // 128-row ones (twice the workgroups)
             const uint64_t wg256 = (uint64_t)units * (((uint64_t)N + 255) / 256);
             block_m = wg256 >= 2 * 256 ? 256 : 128;
             block_n = 64;
         }
+    }
+    if (w64) {
+        const fa::KernelEntry* w = dtype == FA_DTYPE_BF16 ? fa::kBf16W64Kernels : fa::kF16W64Kernels;
         for (int i = 0; i < fa::kNumW64Kernels; ++i)
             if (w[i].d == d && w[i].causal == causal && w[i].block_m == block_m && w[i].block_n == block_n)
                 return &w[i];

@@ -29,6 +29,8 @@ struct FwdParams {
 };
 
 using Launcher = hipError_t (*)(const FwdParams&, hipStream_t);
+// Compute units of the current device (cached per device), 0 when there is none.
+int device_cus();
 // Workgroups of a launch that walks several query tiles per workgroup, or 0 for one
 // workgroup per query tile (units = B * Hq, ntiles = query tiles per head).
 using Blocks = long long (*)(long long units, long long ntiles, int causal);

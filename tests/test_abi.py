@@ -110,13 +110,16 @@ def test_invalid_arguments_are_rejected_before_any_hip_call(lib, kw, code):
 
 def test_stamp_slots_count_the_waves_of_the_default_tile(lib):
     for dtype in (1, 2):
-        # d = 128: 128 query rows per workgroup, 2 waves of 64 rows
-        assert lib.fa_fwd_stamp_slots(2, 32, 4096, 128, dtype) == 2 * 32 * (4096 // 128) * 2
-        assert lib.fa_fwd_stamp_slots(1, 3, 200, 128, dtype) == 3 * 2 * 2
-        # d = 64 the same: a grid this small takes 128-row workgroups of 2 waves
-        assert lib.fa_fwd_stamp_slots(1, 3, 1, 64, dtype) == 3 * 2
-        assert lib.fa_fwd_stamp_slots(1, 3, 300, 64, dtype) == 3 * 3 * 2
-        assert lib.fa_fwd_stamp_slots(0, 3, 100, 64, dtype) == 0
+        for d in (64, 128):
+            # enough rows for 1024 waves of 64 and 512 workgroups of 256: 4 waves of 64 rows
+            assert lib.fa_fwd_stamp_slots(2, 32, 4096, d, dtype) == 2 * 32 * (4096 // 256) * 4
+            # 1024 waves of 64 but only 256 workgroups of 256: 128-row workgroups, 2 waves of 64
+            assert lib.fa_fwd_stamp_slots(1, 8, 8192, d, dtype) == 8 * (8192 // 128) * 2
+            # fewer than 1024 waves of 64 (the SIMDs of a 256-CU device): the 32-rows-per-wave
+            # kernel, 128-row workgroups of 4 waves
+            assert lib.fa_fwd_stamp_slots(1, 3, 200, d, dtype) == 3 * 2 * 4
+            assert lib.fa_fwd_stamp_slots(1, 3, 1, d, dtype) == 3 * 1 * 4
+            assert lib.fa_fwd_stamp_slots(0, 3, 100, d, dtype) == 0
     assert lib.fa_fwd_stamp_slots(1, 1, 64, 64, 0) == -1      # fp32 kernels carry no stamps
     assert lib.fa_fwd_stamp_slots(1, 1, 64, 96, 1) == -1
     assert lib.fa_fwd_stamp_slots(1, 0, 64, 64, 1) == -1

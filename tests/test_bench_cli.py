@@ -8,6 +8,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+from flashattention_online_softmax_fwd_amd import inputs as fin  # noqa: E402
 
 
 @pytest.mark.parametrize("n", [2, 4, 8])
@@ -83,3 +84,23 @@ def test_oracle_leg_uses_each_dtypes_parity_bar():
     assert not tolerances.within(np.array([np.nan, 0, 0]), r, "bf16")
     src = open(os.path.join(ROOT, "bench.py")).read()
     assert "tolerances.within(go, ro, w.dtype)" in src
+
+
+def test_bench_names_the_kernel_the_library_dispatches():
+    """bench.forward_kernel mirrors the library's default choice; the stamp slots the library
+    reserves (workgroups x waves, no walk without a GPU) tell the kernels apart."""
+    from flashattention_online_softmax_fwd_amd import _lib
+    lib = _lib.load()
+    for name, w in fin.WORKLOADS.items():
+        if w.dtype == "f32":
+            continue
+        src, kname = bench.forward_kernel(w, 1024)
+        code = {"bf16": _lib.FA_DTYPE_BF16, "f16": _lib.FA_DTYPE_F16}[w.dtype]
+        units = w.B * w.Hq
+        if src == "w64":
+            nw = int(kname.split(",")[2])
+            rows = 64 * nw
+        else:
+            nw, rows = 4, 128
+        want = units * ((w.N + rows - 1) // rows) * nw
+        assert lib.fa_fwd_stamp_slots(w.B, w.Hq, w.N, w.d, code) == want, (name, src, kname)
