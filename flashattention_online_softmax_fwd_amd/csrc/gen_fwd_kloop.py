@@ -430,6 +430,125 @@ def t(n):
     return TMP0 + n
 
 
+MASK_SGPRS = {0: ["vcc", "%[mk1]", "%[mk2]", "%[mk3]"], 1: ["%[mk4]", "%[mk5]", "%[mk6]", "%[mk7]"]}
+
+
+def mask_ops(s, m, mask_sgpr):
+    """-inf into the scores S(s..s+15) of keys past the diagonal ("tri", threshold %[dmask]) or
+    past the valid count ("lim", %[dlim]); nothing when m is None."""
+    o = []
+    if not m:
+        return o
+    thr = "%[dmask]" if m == "tri" else "%[dlim]"
+    # key index within the half of register r of this lane, minus 4*hi: 8*(r>>2) + (r&3)
+    seq = []
+    for r in range(16):
+        kc = 8 * (r >> 2) + (r & 3)
+        mk = mask_sgpr[r % 4]
+        if mk == "vcc":
+            cmp_ = Ins("v_cmp_le_i32_e32 vcc, %d, %s" % (kc, thr), "cmps", defs=["vcc"])
+            sel = Ins("v_cndmask_b32_e32 %s, %s, %s, vcc" % (vr(s + r), vr(NEGINF), vr(s + r)), "valu",
+                      defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), "vcc"])
+        else:
+            cmp_ = Ins("v_cmp_le_i32_e64 %s, %d, %s" % (mk, kc, thr), "cmps", defs=[mk])
+            sel = Ins("v_cndmask_b32_e64 %s, %s, %s, %s" % (vr(s + r), vr(NEGINF), vr(s + r), mk), "valu",
+                      defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), mk])
+        seq.append((cmp_, sel))
+    for r in range(16):
+        o.append(seq[r][0])
+        if r >= 3:
+            o.append(seq[r - 3][1])
+    for r in range(13, 16):
+        o.append(seq[r][1])
+    return o
+
+
+def interleave_streams(ops_dead, streams, live):
+    out = list(ops_dead)
+    ls = [streams[rb] for rb in live]
+    i = 0
+    while any(i < len(x) for x in ls):
+        for x in ls:
+            if i < len(x):
+                out.append(x[i])
+        i += 1
+    return out
+
+
+def softmax_fast(g, sbuf, pbuf, par, masks, dead):
+    """The vector work of one half when every row's reference is finite, split in two.
+
+    fast: the masks, then P = exp2(S c - m) against the current reference into temporaries
+    (S stays as it is), P rounded for the PV product, the row sums in the four chains of
+    softmax_ops, l_old = l, l += sum, and the wave's ballot %[ga<par>] of lanes whose partial
+    sum exceeds 2^slack: some score may have outrun the reference.
+    slow (run only when that ballot is set): l = l_old, then softmax_ops on the masked S,
+    which moves the reference, recomputes P and sets %[ga<par>] to its own ballot.
+    When no row's maximum outruns its reference by the slack, softmax_ops would keep the
+    reference and use alpha = 1, so both paths give the same bits."""
+    live = [rb for rb in (0, 1) if rb not in dead]
+    ops_dead = []
+    for rb in dead:
+        for ks in range(2):
+            for j in range(4):
+                ops_dead.append(Ins("v_mov_b32 %s, 0" % vr(Pr(pbuf, rb, ks) + j), "valu", defs=[vr(Pr(pbuf, rb, ks) + j)]))
+    limit = "0x57800000" if g.elem == "bf16" else "0x47000000"      # 2^48, 2^15: 2^slack
+    streams = {rb: [] for rb in live}
+    checks = []
+    restore = []
+    for idx, rb in enumerate(live):
+        o = streams[rb]
+        s = Sr(sbuf, rb)
+        base = 9 * idx       # t(0..8) and t(9..17): the blocks' temporaries live side by side
+        T = lambda n, base=base: vr(t(base + n))
+        S = lambda r, s=s: vr(s + r)
+        m = vr(Mr(rb))
+        o.extend(mask_ops(s, masks.get(rb), MASK_SGPRS[rb]))
+        adds_late = []
+        for c in range(8):
+            a, b = (T(0), T(1)) if c % 2 == 0 else (T(2), T(3))
+            o.append(Ins("v_fma_f32 %s, %s, %%[c], -%s" % (a, S(2 * c), m), "valu", defs=[a], uses=[S(2 * c), m]))
+            o.append(Ins("v_fma_f32 %s, %s, %%[c], -%s" % (b, S(2 * c + 1), m), "valu", defs=[b], uses=[S(2 * c + 1), m]))
+            o.append(Ins("v_exp_f32_e32 %s, %s" % (a, a), "trans", defs=[a], uses=[a]))
+            o.append(Ins("v_exp_f32_e32 %s, %s" % (b, b), "trans", defs=[b], uses=[b]))
+            p = Pr(pbuf, rb, c // 4) + c % 4
+            o.append(Ins("%s %s, %s, %s" % (g.cvt_op, vr(p), a, b), "valu", defs=[vr(p)], uses=[a, b]))
+            if c < 4:
+                # chains 0..3 start with elements (2c, 2c + 1), as in softmax_ops
+                o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + c), a, b), "valu", defs=[T(5 + c)], uses=[a, b]))
+            else:
+                # element r >= 8 joins chain r % 4, in the order of softmax_ops
+                for r, x in ((2 * c, a), (2 * c + 1, b)):
+                    o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5 + r % 4), x, T(5 + r % 4)), "valu",
+                                 defs=[T(5 + r % 4)], uses=[x, T(5 + r % 4)]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5), T(5), T(6)), "valu", defs=[T(5)], uses=[T(5), T(6)]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(7), T(7), T(8)), "valu", defs=[T(7)], uses=[T(7), T(8)]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (T(5), T(5), T(7)), "valu", defs=[T(5)], uses=[T(5), T(7)]))
+        L = vr(Lr(rb))
+        o.append(Ins("v_mov_b32_e32 %s, %s" % (T(4), L), "valu", defs=[T(4)], uses=[L]))
+        o.append(Ins("v_add_f32_e32 %s, %s, %s" % (L, L, T(5)), "valu", defs=[L], uses=[L, T(5)]))
+        gb = "%%[g%d%d]" % (par, rb)
+        checks += [Ins("v_cmp_lt_f32_e32 vcc, %s, %s" % (limit, T(5)), "cmps", defs=["vcc"], uses=[T(5)]),
+                   Ins("s_mov_b64 %s, vcc" % gb, "salu", defs=[gb], uses=["vcc"])]
+        restore.append(Ins("v_mov_b32_e32 %s, %s" % (L, T(4)), "valu", defs=[L], uses=[T(4)]))
+    fast = interleave_streams(ops_dead, streams, live) + checks
+    gs = ["%%[g%d%d]" % (par, rb) for rb in live]
+    if len(gs) == 2:
+        fast.append(Ins("s_or_b64 %%[ga%d], %s, %s" % (par, gs[0], gs[1]), "salu", defs=["%%[ga%d]" % par], uses=gs))
+    else:
+        fast.append(Ins("s_mov_b64 %%[ga%d], %s" % (par, gs[0]), "salu", defs=["%%[ga%d]" % par], uses=gs))
+    slow = restore + softmax_ops(g, sbuf, pbuf, par, {}, False, dead)
+    return fast, slow, par
+
+
+def soft(g, sbuf, pbuf, par, masks, first, dead):
+    """The softmax of a half: the two-path form once every reference is finite (and with the
+    fp32 row sums), else softmax_ops."""
+    if FAST and not first and not MFMA_ROWSUM:
+        return softmax_fast(g, sbuf, pbuf, par, masks, dead)
+    return softmax_ops(g, sbuf, pbuf, par, masks, first, dead)
+
+
 def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
     """The vector work of one half.
 
@@ -446,36 +565,14 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
             for j in range(4):
                 ops_dead.append(Ins("v_mov_b32 %s, 0" % vr(Pr(pbuf, rb, ks) + j), "valu", defs=[vr(Pr(pbuf, rb, ks) + j)]))
         ops_dead.append(Ins("v_mov_b32 %s, 1.0" % vr(ALr(par, rb)), "valu", defs=[vr(ALr(par, rb))]))
-    mask_sgprs = {0: ["vcc", "%[mk1]", "%[mk2]", "%[mk3]"], 1: ["%[mk4]", "%[mk5]", "%[mk6]", "%[mk7]"]}
+    mask_sgprs = MASK_SGPRS
     for idx, rb in enumerate(live):
         mask_sgpr = mask_sgprs[rb]
         o = streams[rb]
         s = Sr(sbuf, rb)
         base = 8 * idx       # temporaries of this row block: t(base) .. t(base + 8)
         T = lambda n: vr(t(base + n))
-        m = masks.get(rb)
-        if m:
-            thr = "%[dmask]" if m == "tri" else "%[dlim]"
-            # key index within the half of register r of this lane, minus 4*hi: 8*(r>>2) + (r&3)
-            seq = []
-            for r in range(16):
-                kc = 8 * (r >> 2) + (r & 3)
-                mk = mask_sgpr[r % 4]
-                if mk == "vcc":
-                    cmp_ = Ins("v_cmp_le_i32_e32 vcc, %d, %s" % (kc, thr), "cmps", defs=["vcc"])
-                    sel = Ins("v_cndmask_b32_e32 %s, %s, %s, vcc" % (vr(s + r), vr(NEGINF), vr(s + r)), "valu",
-                              defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), "vcc"])
-                else:
-                    cmp_ = Ins("v_cmp_le_i32_e64 %s, %d, %s" % (mk, kc, thr), "cmps", defs=[mk])
-                    sel = Ins("v_cndmask_b32_e64 %s, %s, %s, %s" % (vr(s + r), vr(NEGINF), vr(s + r), mk), "valu",
-                              defs=[vr(s + r)], uses=[vr(s + r), vr(NEGINF), mk])
-                seq.append((cmp_, sel))
-            for r in range(16):
-                o.append(seq[r][0])
-                if r >= 3:
-                    o.append(seq[r - 3][1])
-            for r in range(13, 16):
-                o.append(seq[r][1])
+        o.extend(mask_ops(s, masks.get(rb), mask_sgprs[rb]))
         # row max over this lane's 16 scores
         S = lambda r: vr(s + r)
         o.append(Ins("v_max3_f32 %s, %s, %s, %s" % (T(0), S(0), S(1), S(2)), "valu", defs=[T(0)], uses=[S(0), S(1), S(2)]))
@@ -544,14 +641,7 @@ def softmax_ops(g, sbuf, pbuf, par, masks, first, dead):
         o.append(Ins("v_fma_f32 %s, %s, %s, %s" % (vr(Lr(rb)), vr(Lr(rb)), vr(ALr(par, rb)), T(5)), "valu",
                      defs=[vr(Lr(rb))], uses=[vr(Lr(rb)), vr(ALr(par, rb)), T(5)]))
     # interleave the row blocks' streams
-    out = list(ops_dead)
-    ls = [streams[rb] for rb in live]
-    i = 0
-    while any(i < len(x) for x in ls):
-        for x in ls:
-            if i < len(x):
-                out.append(x[i])
-        i += 1
+    out = interleave_streams(ops_dead, streams, live)
     # the wave's "any row moved its reference" ballot for this parity
     gs = ["%%[g%d%d]" % (par, rb) for rb in live]
     if len(gs) == 2:
@@ -685,6 +775,7 @@ def half_groups(g, s_next, pv_prev):
 
 
 LEAD = 2          # product groups a group's operand reads run ahead
+FAST = os.environ.get("FA_GEN_FAST", "1") == "1"
 HEAD_VALU = 12    # softmax instructions that cover the first reads of a half after a barrier
 
 
@@ -710,8 +801,14 @@ def half_interleaved(g, s_next, pv_prev, soft, rescale_par, extra=(), preissued=
         out.append(Skip("%%[ga%d]" % rescale_par, rescale_block(rescale_par, pv_prev[2]), "L_rs%d" % len(g.labels)))
         g.labels.append(1)
     nxt = first_reads(g, *next_half) if next_half else ()
+    slow = None
+    if isinstance(soft, tuple):
+        soft, slow, par = soft
     out.extend(merge_half([merged], list(soft), list(extra), lead=LEAD, preissued=LEAD if preissued else 0,
                           head_valu=HEAD_VALU if after_barrier else 0, next_reads=nxt))
+    if slow is not None:
+        out.append(Skip("%%[ga%d]" % par, slow, "L_sl%d" % len(g.labels)))
+        g.labels.append(1)
     return out
 
 
@@ -739,10 +836,8 @@ def build(elem, causal, nw):
         prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
     if MFMA_ROWSUM:
         prog.extend(ones16(elem))
-    prog.append(Ins("s_waitcnt vmcnt(0)", "wait"))
-    for r in range(8 * KK()):
-        prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
-    # ---- first tiles: K(0), K(1) (if any), V(0)
+    # ---- first tiles: K(0), K(1) (if any), V(0), in flight together with the Q loads: the
+    # barrier's wait covers both
     prog.extend(dma_tile("k", nw))
     prog.extend(advance_k())
     prog.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k", nw), "L_k1"))
@@ -750,6 +845,8 @@ def build(elem, causal, nw):
     prog.extend(dma_tile("v", nw))
     prog.extend(advance_v())
     prog.extend(barrier())
+    for r in range(8 * KK()):
+        prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
     # S(0) alone
     prog.extend(merge_half([g.s_stream(0, 0, all_rb)], [], []))
 
@@ -778,16 +875,16 @@ def build(elem, causal, nw):
     # ---- L >= 1 path: half 0 unmasked
     pathA = []
     pathA.extend(half_interleaved(g, (1, 1, all_rb), None,
-                                  softmax_ops(g, 0, 0, 0, {}, True, ()), None))
+                                  soft(g, 0, 0, 0, {}, True, ()), None))
     pathA.append(Ins("s_mov_b64 %[ga0], 0", "salu", defs=["%[ga0]"]))      # O is zero: no rescale
     # steady loop over k = 1 .. L-1
     head, dmas = iter_head(False, False)
     body = list(head)
     body.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
-                                 softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas,
+                                 soft(g, 1, 1, 1, {}, False, ()), 0, dmas,
                                  next_half=((1, 1, all_rb), (1, 1, all_rb)), after_barrier=True))
     body.extend(half_interleaved(g, (1, 1, all_rb), (1, 1, all_rb),
-                                 softmax_ops(g, 0, 0, 0, {}, False, ()), 1, [], preissued=True))
+                                 soft(g, 0, 0, 0, {}, False, ()), 1, [], preissued=True))
     body.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     pathA.append(Ins("s_sub_u32 %[cnt], %[last], 1", "salu", defs=["%[cnt]"]))
     pathA.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", body, "L_loop")], "L_skiploop"))
@@ -796,17 +893,17 @@ def build(elem, causal, nw):
     pathA.extend(head)
     pathA.extend(lim_ops("limA"))
     pathA.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
-                                  softmax_ops(g, 1, 1, 1, {}, False, ()), 0, dmas,
+                                  soft(g, 1, 1, 1, {}, False, ()), 0, dmas,
                                   next_half=((1, 1, rbB), (1, 1, all_rb)), after_barrier=True))
     pathA.extend(half_interleaved(g, (1, 1, rbB), (1, 1, all_rb),
-                                  softmax_ops(g, 0, 0, 0, maskA, False, ()), 1, [], preissued=True))
+                                  soft(g, 0, 0, 0, maskA, False, ()), 1, [], preissued=True))
     pathA.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     pathA.append(Ins("s_branch L_tailB_%=", "branch"))
     # ---- L == 0 path: half 0 masked A
     pathB = []
     pathB.extend(lim_ops("limA"))
     pathB.extend(half_interleaved(g, (1, 1, rbB), None,
-                                  softmax_ops(g, 0, 0, 0, maskA, True, ()), None))
+                                  soft(g, 0, 0, 0, maskA, True, ()), None))
     pathB.append(Ins("s_mov_b64 %[ga0], 0", "salu", defs=["%[ga0]"]))
     # ---- tail B (iteration L+1): half 2L+1 (PV(2L), softmax masked B), half 2L+2 (PV(2L+1))
     tail = []
@@ -814,7 +911,7 @@ def build(elem, causal, nw):
     tail.extend(head)
     tail.extend(lim_ops("limB"))
     tail.extend(half_interleaved(g, None, (0, 0, all_rb),
-                                 softmax_ops(g, 1, 1, 1, maskB, False, deadB), 0, dmas,
+                                 soft(g, 1, 1, 1, maskB, False, deadB), 0, dmas,
                                  next_half=(None, (1, 1, rbB)), after_barrier=True))
     tail.extend(half_interleaved(g, None, (1, 1, rbB), [], 1, [], preissued=True))
     tail.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
