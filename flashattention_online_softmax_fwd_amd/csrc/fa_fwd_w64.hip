@@ -164,7 +164,7 @@ fwd_w64_kernel(const FwdParams p)
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)ldsb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
     // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
-    // step and dims 32dt + 16(G&1) + 4s ..; buffer V1 to start (the walk flips to V0 first).
+    // step and dims 32dt + 16(G&1) + 4s ..; buffer V0 to start (V tile 0 lands in V1).
     const int G = lane >> 4;
     const int jj = (lane >> 2) & 3;
     const int ss = lane & 3;
@@ -176,7 +176,7 @@ fwd_w64_kernel(const FwdParams p)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
-            voff[(D / 32) * r + dt] = (int)ldsb + 3 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+            voff[(D / 32) * r + dt] = (int)ldsb + 2 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
         }
     }
     // Tile loads: slice ii = wave + NW i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
@@ -203,7 +203,9 @@ fwd_w64_kernel(const FwdParams p)
     const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
 
-    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 2 * TILE + 1024 * wave;
+    // K tile j lands in K buffer j % 2, V tile j in V buffer (j + 1) % 2; the operand reads
+    // start at buffer 0 of each and flip before every tile (V tile j is read one tile later)
+    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 3 * TILE + 1024 * wave;
     unsigned soff, kit, cnt;
     unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
     int dlim;

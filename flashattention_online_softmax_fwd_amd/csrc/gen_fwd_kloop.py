@@ -351,6 +351,8 @@ def lower(items, st, out, uid):
 class Gen:
     def __init__(self, elem, causal):
         self.elem = elem            # "bf16" or "f16"
+        self.kbuf = 0               # 1: operand reads go to the K / V buffer above the one
+        self.vbuf = 0               #    %[koff] / %[voff] point at (the unrolled steady loop)
         self.causal = causal
         self.mfma_op = "v_mfma_f32_32x32x16_" + elem
         self.mfma16_op = "v_mfma_f32_16x16x32_" + elem
@@ -363,13 +365,16 @@ class Gen:
 
     # ---- operand reads from LDS
     def k_read(self, i, kk, t):
-        """K operand for dims 16kk.. of keys 32t.. of the current K tile into staging i."""
-        return Ins("ds_read_b128 %s, %%[koff%d] offset:%d" % (vrange(KST(i), 4), kk, 32 * ROWB() * t), "lds",
+        """K operand for dims 16kk.. of keys 32t.. of the current K tile into staging i (the tile
+        in the buffer %[koff] points at, or in the other one when self.kbuf is set)."""
+        off = 32 * ROWB() * t + self.kbuf * TILE()
+        return Ins("ds_read_b128 %s, %%[koff%d] offset:%d" % (vrange(KST(i), 4), kk, off), "lds",
                    defs=regs(KST(i), 4))
 
     def v_reads(self, i, db, ks, t):
-        """V^T operand of dims 32db.. and keys 32t + 16ks.. (two transposing reads)."""
-        off = 32 * ROWB() * t + 16 * ROWB() * ks
+        """V^T operand of dims 32db.. and keys 32t + 16ks.. (two transposing reads; self.vbuf as
+        self.kbuf)."""
+        off = 32 * ROWB() * t + 16 * ROWB() * ks + self.vbuf * TILE()
         return [Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i), 2), db, off), "lds",
                     defs=regs(VST(i), 2)),
                 Ins("ds_read_b64_tr_b16 %s, %%[voff%d] offset:%d" % (vrange(VST(i) + 2, 2), DB() + db, off), "lds",
@@ -859,8 +864,8 @@ def build(elem, causal, nw):
         Ins("v_sub_u32_e32 %%[dlim], %%[%s], %%[hi4]" % which, "valu", defs=["%[dlim]"])]
 
     # iteration k: barrier B_k, loads K(k+1) and V(k), halves 2k-1 and 2k
-    def iter_head(cond_k, cond_v):
-        out = toggle_reads()
+    def iter_head(cond_k, cond_v, toggle=True):
+        out = toggle_reads() if toggle else []
         out.extend(barrier())
         ek = dma_tile("k", nw) + advance_k()
         ev = dma_tile("v", nw) + advance_v()
@@ -877,17 +882,31 @@ def build(elem, causal, nw):
     pathA.extend(half_interleaved(g, (1, 1, all_rb), None,
                                   soft(g, 0, 0, 0, {}, True, ()), None))
     pathA.append(Ins("s_mov_b64 %[ga0], 0", "salu", defs=["%[ga0]"]))      # O is zero: no rescale
-    # steady loop over k = 1 .. L-1
-    head, dmas = iter_head(False, False)
-    body = list(head)
-    body.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
-                                 soft(g, 1, 1, 1, {}, False, ()), 0, dmas,
-                                 next_half=((1, 1, all_rb), (1, 1, all_rb)), after_barrier=True))
-    body.extend(half_interleaved(g, (1, 1, all_rb), (1, 1, all_rb),
-                                 soft(g, 0, 0, 0, {}, False, ()), 1, [], preissued=True))
-    body.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+    # steady loop over k = 1 .. L-1.  K tile j lands in K buffer j % 2 and V tile j in V buffer
+    # (j + 1) % 2; %[koff] and %[voff] start at buffer 0 of each and each toggling iteration
+    # flips both before reading, so iteration k reads K buffer k % 2 (tile k) and V buffer
+    # k % 2 (tile k - 1).  Pairs of iterations run with the buffer named by the reads' offsets
+    # (no register toggles); an odd count ends with one iteration in the toggling form, which
+    # leaves the registers as L - 1 toggles would.
+    def iteration(toggle, kbuf=0, vbuf=0):
+        g.kbuf, g.vbuf = kbuf, vbuf
+        head, dmas = iter_head(False, False, toggle)
+        out = list(head)
+        out.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
+                                    soft(g, 1, 1, 1, {}, False, ()), 0, dmas,
+                                    next_half=((1, 1, all_rb), (1, 1, all_rb)), after_barrier=True))
+        out.extend(half_interleaved(g, (1, 1, all_rb), (1, 1, all_rb),
+                                    soft(g, 0, 0, 0, {}, False, ()), 1, [], preissued=True))
+        out.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
+        g.kbuf = g.vbuf = 0
+        return out
+
+    pair = iteration(False, 1, 1) + iteration(False, 0, 0)
     pathA.append(Ins("s_sub_u32 %[cnt], %[last], 1", "salu", defs=["%[cnt]"]))
-    pathA.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", body, "L_loop")], "L_skiploop"))
+    pathA.append(Ins("s_lshr_b32 %[cnt], %[cnt], 1", "salu", defs=["%[cnt]"], uses=["%[cnt]"]))
+    pathA.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", pair, "L_loop")], "L_skiploop"))
+    pathA.append(Cond(["s_bitcmp0_b32 %[last], 0"], iteration(True), "L_odd%d" % len(g.labels)))
+    g.labels.append(1)
     # iteration L: half 2L-1 unmasked, half 2L masked A
     head, dmas = iter_head(True, False)
     pathA.extend(head)
