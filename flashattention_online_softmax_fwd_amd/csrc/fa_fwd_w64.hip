@@ -27,11 +27,14 @@
 //
 // 256-row workgroups walk pairs of query tiles (the heaviest causal tile of a head with its
 // lightest) when that balances as well as one tile per workgroup: one workgroup per CU,
-// no dispatch gaps, and every CU gets the same causal work.
+// no dispatch gaps, and every CU gets the same causal work.  Each item (query tile) of the
+// walk loads the next one's first K/V tiles and stages its Q rows in LDS during its own last
+// two steps, so the next item starts without waiting for memory.
 //
-// LDS (4 tiles: 64 KiB at d = 128, 32 KiB at d = 64): K tiles at +0 and +TILE, V tiles at
-// +2 TILE and +3 TILE, each [64 keys][d] with 16-byte chunks XOR-swizzled per row (the layout
-// of fa_fwd_mfma16.hip), filled by buffer_load_dwordx4 ... lds.  Rows past N read as zero and
+// LDS: sets of 4 tiles (64 KiB at d = 128, 32 KiB at d = 64; two sets for 256-row workgroups,
+// used by consecutive items in turn): K tiles at +0 and +TILE, V tiles at +2 TILE and
+// +3 TILE, each [64 keys][d] with 16-byte chunks XOR-swizzled per row (the layout of
+// fa_fwd_mfma16.hip), filled by buffer_load_dwordx4 ... lds.  Rows past N read as zero and
 // rows of O and LSE past N are not written: every buffer range ends at the head's last row.
 #include "fa_kernels.h"
 #include "fa_mfma16_common.h"
@@ -85,9 +88,12 @@ fwd_w64_kernel(const FwdParams p)
     constexpr int BM = R * NW;        // query rows of the workgroup
     constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
     constexpr int RPS = 1024 / ROWB;  // rows per 1 KiB load slice
-    // K0, K1, V0, V1 at 0, TILE, 2 TILE, 3 TILE.  Aligned to 32 KiB: the walk switches buffers
-    // by flipping the TILE bit of the addresses.
-    __shared__ __attribute__((aligned(32768))) char lds[4 * TILE];
+    // Two sets of four tiles, set s at 4 s TILE: K0, K1, V0, V1 at +0, +TILE, +2 TILE, +3 TILE.
+    // Consecutive items of a workgroup use the two sets in turn, so that an item's last steps can
+    // load the next item's first tiles.  Aligned to 32 KiB: the walk switches buffers by flipping
+    // the TILE bit of the addresses.  128-row workgroups run one item and use the first set.
+    constexpr int SETS = NW == 4 ? 2 : 1;
+    __shared__ __attribute__((aligned(32768))) char lds[SETS * 4 * TILE];
 
     const int N = p.N;
     const int units = p.B * p.Hq;
@@ -103,11 +109,11 @@ fwd_w64_kernel(const FwdParams p)
         real0 = __builtin_amdgcn_s_memrealtime();
         cyc0 = __builtin_amdgcn_s_memtime();
     }
-    // Walk: the workgroup takes pairs j, j + G, ... of the units * ceil(nqt / 2) pairs; pair j
-    // is query tiles nqt - 1 - i and i (i = j mod the pairs per head) of one head, whose
-    // causal work adds up to the same for every i.  With the XCD map, logical workgroup ids
-    // run down each XCD in turn, so the pairs of a head (and of heads sharing K/V) stay in one
-    // L2.  Without the walk, one query tile per workgroup.
+    // Items: query tiles.  With the walk, the workgroup takes pairs j, j + G, ... of the units *
+    // ceil(nqt / 2) pairs; pair j is query tiles nqt - 1 - i and i (i = j mod the pairs per head)
+    // of one head, whose causal work adds up to the same for every i.  With the XCD map, logical
+    // workgroup ids run down each XCD in turn, so the pairs of a head (and of heads sharing K/V)
+    // stay in one L2.  Without the walk, one query tile per workgroup.
     const int per_head = (nqt + 1) >> 1;
     int j = 0, jstep = 1, jend = 1;
     if (p.walk) {
@@ -116,19 +122,12 @@ fwd_w64_kernel(const FwdParams p)
         jstep = G;
         jend = units * per_head;
     }
-#pragma nounroll
-    for (; j < jend; j += jstep)
-#pragma nounroll
-    for (int s = 0; s < 2; ++s) {
-    int bh, qt;
-    if (p.walk) {
-        bh = j / per_head;
-        const int i = j - bh * per_head;
-        if (s == 1 && i == nqt - 1 - i) break;      // the middle tile of an odd count
-        qt = s == 0 ? nqt - 1 - i : i;
-    } else {
-        if (s == 1) break;
-        if (p.xcd_map) {
+    auto tile_of = [&](int jj, int ss, int& bh, int& qt) {
+        if (p.walk) {
+            bh = jj / per_head;
+            const int i = jj - bh * per_head;
+            qt = ss == 0 ? nqt - 1 - i : i;
+        } else if (p.xcd_map) {
             int t;
             xcd_order(bid, units, nqt, bh, t);
             qt = CAUSAL ? nqt - 1 - t : t;   // longest first
@@ -136,7 +135,57 @@ fwd_w64_kernel(const FwdParams p)
             bh = bid % units;
             qt = CAUSAL ? nqt - 1 - bid / units : bid / units;
         }
+    };
+    auto next_of = [&](int& jj, int& ss) {
+        if (p.walk && ss == 0) {
+            const int i = jj - (jj / per_head) * per_head;
+            if (i != nqt - 1 - i) {          // the middle tile of an odd count has no partner
+                ss = 1;
+                return;
+            }
+        }
+        jj += jstep;
+        ss = 0;
+    };
+    const int range = N * ROWB;
+    auto rsrc = [&](const void* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+    };
+    const unsigned ldsb = (unsigned)(uintptr_t)(FA_LDS char*)lds;
+    // Tile loads: slice ii = wave + NW i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
+    // lane's 16 bytes are row RPS ii + lane / CPR, physical chunk lane % CPR, i.e. logical chunk
+    // (lane % CPR) ^ swz(row).  ii enters the swizzle only through ii mod 4 (d = 128) or ii mod 2
+    // (d = 64): two patterns (i even, odd; the same one when NW = 4).
+    int dma[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int row = RPS * (wave + NW * e) + lane / CPR;
+        dma[e] = 1024 * wave + (lane / CPR) * ROWB + 16 * ((lane % CPR) ^ swz<D>(row));
     }
+    const int dmask = l32 - 4 * hi;   // causal: key 8(r>>2) + (r&3) + 4hi of a diagonal half visible iff <= row l32
+    const int hi4 = 4 * hi;
+    // A negative scale is folded into Q's sign; a zero scale becomes the smallest normal.
+    const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
+    const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
+    // The item's rows, O rows and key tiles.
+    auto key_tiles = [&](int qt) {
+        const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
+        return (kv_end + 63) / 64;
+    };
+
+    int s = 0, set = 0;
+    unsigned pf = 0;                 // 1: this item's first tiles and Q were loaded by the item before
+    int qlds = 0;                    // then: this lane's 16 bytes of the staged Q
+#pragma nounroll
+    while (j < jend) {
+    int bh, qt;
+    tile_of(j, s, bh, qt);
+    int jn = j, sn = s;
+    next_of(jn, sn);
+    const bool has_next = jn < jend;
+    int bhn = bh, qtn = qt;
+    if (has_next) tile_of(jn, sn, bhn, qtn);
+
     const int b = bh / p.Hq;
     const int hk = (bh - b * p.Hq) / p.group;
     const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
@@ -144,25 +193,32 @@ fwd_w64_kernel(const FwdParams p)
     const char* Qh = (const char*)p.q + (size_t)bh * N * ROWB;
     char* Oh = (char*)p.o + (size_t)bh * N * ROWB;
     float* Lh = p.lse + (size_t)bh * N;
-    const int range = N * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)Oh, (short)0, range, 0x00020000);
-    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc((void*)Lh, (short)0, N * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t krs = rsrc(Kh, range);
+    const __amdgpu_buffer_rsrc_t vrs = rsrc(Vh, range);
+    const __amdgpu_buffer_rsrc_t qrs = rsrc(Qh, range);
+    const __amdgpu_buffer_rsrc_t ors = rsrc(Oh, range);
+    const __amdgpu_buffer_rsrc_t lrs = rsrc(Lh, N * 4);
+    // the next item's head (its K/V tiles and Q rows are loaded in this item's last steps)
+    const int bn = bhn / p.Hq;
+    const int hkn = (bhn - bn * p.Hq) / p.group;
+    const __amdgpu_buffer_rsrc_t nkrs = rsrc((const char*)p.k + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
+    const __amdgpu_buffer_rsrc_t nvrs = rsrc((const char*)p.v + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
+    const __amdgpu_buffer_rsrc_t nqrs = rsrc((const char*)p.q + (size_t)bhn * N * ROWB, range);
 
     const int q0 = qt * BM;
     const int row0 = q0 + R * wave;                     // the wave's first query row
     const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
     const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
     const int loff = (row0 + l32) * 4;
-    const unsigned ldsb = (unsigned)(uintptr_t)(FA_LDS char*)lds;
+    const int nqoff = (qtn * BM + R * wave + l32) * ROWB + 16 * hi;
+    const unsigned setb = ldsb + (unsigned)(set * 4 * TILE);
+    const unsigned nsetb = ldsb + (unsigned)((set ^ (SETS - 1)) * 4 * TILE);
 
     // K operand: row l32 of the 32-key block, logical chunk 2kk + hi (buffer K0 to start).
     const int kx = swz<D>(l32);
     int koff[8] = {};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)ldsb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
+    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)setb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
     // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
     // step and dims 32dt + 16(G&1) + 4s ..; buffer V0 to start (V tile 0 lands in V1).
     const int G = lane >> 4;
@@ -176,36 +232,35 @@ fwd_w64_kernel(const FwdParams p)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
-            voff[(D / 32) * r + dt] = (int)ldsb + 2 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+            voff[(D / 32) * r + dt] = (int)setb + 2 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
         }
     }
-    // Tile loads: slice ii = wave + NW i of a tile holds LDS bytes [1024 ii, 1024 ii + 1024); this
-    // lane's 16 bytes are row RPS ii + lane / CPR, physical chunk lane % CPR, i.e. logical chunk
-    // (lane % CPR) ^ swz(row).  ii enters the swizzle only through ii mod 4 (d = 128) or ii mod 2
-    // (d = 64): two patterns (i even, odd; the same one when NW = 4).
-    int dma[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int row = RPS * (wave + NW * e) + lane / CPR;
-        dma[e] = 1024 * wave + (lane / CPR) * ROWB + 16 * ((lane % CPR) ^ swz<D>(row));
-    }
-    const int dmask = l32 - 4 * hi;   // causal: key 8(r>>2) + (r&3) + 4hi of a diagonal half visible iff <= row l32
-    const int hi4 = 4 * hi;
 
     // Key tiles of 64 for the workgroup; the last one this wave's rows need.
-    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-    const int nt = (kv_end + 63) / 64;
+    const int nt = key_tiles(qt);
     const int last = CAUSAL ? min(nt - 1, (q0 + R * wave) / 64) : nt - 1;
     const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
     const int limA = valid_last - 1;
     const int limB = valid_last - 33;
-    // A negative scale is folded into Q's sign; a zero scale becomes the smallest normal.
-    const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
-    const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
+    const int nnt = key_tiles(qtn);
+    // The next item's loads: its first K/V tiles at step max(nt - 1, 1) into the other set, its
+    // Q rows at step nt (no S product of this item follows) into this wave's staging area: the
+    // K buffers and the idle V buffer of this set (waves 0-2) or V0 of the other set (wave 3),
+    // none of which this item reads after step nt - 1 or the next one fills before its own Q is read.
+    const unsigned never = 0xffffffffu;
+    const unsigned pkv = has_next ? (unsigned)max(nt - 1, 1) : never;
+    const unsigned pq = has_next ? (unsigned)nt : never;
+    const unsigned nkdst = nsetb + 1024 * wave;
+    unsigned qst;
+    if (wave == 0) qst = setb;
+    else if (wave == 1) qst = setb + TILE;
+    else if (wave == 2) qst = setb + 2 * TILE + ((nt + 1) & 1) * TILE;
+    else qst = nsetb + 2 * TILE;
+    const int qlds_next = (int)qst + 16 * lane;
 
     // K tile j lands in K buffer j % 2, V tile j in V buffer (j + 1) % 2; the operand reads
     // start at buffer 0 of each and flip before every tile (V tile j is read one tile later)
-    unsigned ksrc = 0, kdst = ldsb + 1024 * wave, vsrc = 0, vdst = ldsb + 3 * TILE + 1024 * wave;
+    unsigned ksrc = 0, kdst = setb + 1024 * wave, vsrc = 0, vdst = setb + 3 * TILE + 1024 * wave;
     unsigned soff, kit, cnt;
     unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
     int dlim;
@@ -223,7 +278,9 @@ fwd_w64_kernel(const FwdParams p)
                  : [dma0] "v"(dma[0]), [dma1] "v"(dma[1]), [qoff] "v"(qoff), [ooff] "v"(ooff), [loff] "v"(loff),  \
                    [dmask] "v"(dmask), [hi4] "v"(hi4), [krs] "s"(krs), [vrs] "s"(vrs), [qrs] "s"(qrs),             \
                    [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
-                   [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip)                                                 \
+                   [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip), [pf] "s"(pf), [qlds] "v"(qlds),               \
+                   [pkv] "s"(pkv), [pq] "s"(pq), [nkrs] "s"(nkrs), [nvrs] "s"(nvrs), [nqrs] "s"(nqrs),            \
+                   [nqoff] "v"(nqoff), [nkdst] "s"(nkdst), [nnt] "s"(nnt), [qst] "s"(qst)                        \
                  : CLOBBERS)
 #define FA_W64_ASM(TEXT) FA_W64_ASM_C(TEXT, FA_W64_CLOBBERS)
 #define FA_W64_PICK(W, DD)                                                                 \
@@ -250,8 +307,13 @@ fwd_w64_kernel(const FwdParams p)
 #undef FA_W64_PICK
 #undef FA_W64_ASM
 #undef FA_W64_ASM_C
-    // every wave is done with the LDS tiles before the next item loads its own
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // No barrier here: the next item's first barrier comes before anything it writes to LDS
+    // could reach a tile this item still reads.
+    j = jn;
+    s = sn;
+    set ^= SETS - 1;
+    pf = 1;
+    qlds = qlds_next;
     }
 
     if (p.stamps && lane == 0) {

@@ -764,6 +764,84 @@ def barrier():
     return [Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "waitall"), Ins("s_barrier", "barrier")]
 
 
+def nstores():
+    """Vector memory stores of the epilogue (O and LSE), counted in the instructions it emits:
+    an item's first barrier may leave exactly this many of the item before in flight."""
+    return sum(1 for ins in epilogue(Gen("bf16", False)) if ins.kind == "vstore")
+
+
+def q_vloads():
+    """This wave's Q rows straight into the operand registers (rb 1 sits 32 rows on)."""
+    out = [Ins("s_mov_b32 %%[soff], %d" % (32 * ROWB()), "salu", defs=["%[soff]"])]
+    for rb in (0, 1):
+        for kk in range(KK()):
+            so = "0" if rb == 0 else "%[soff]"
+            out.append(Ins("buffer_load_dwordx4 %s, %%[qoff], %%[qrs], %s offen offset:%d" % (vrange(Qr(rb, kk), 4), so, 32 * kk),
+                           "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else ["%[soff]"]))
+    return out
+
+
+def q_stage():
+    """The next item's Q rows of this wave into its LDS staging area at %[qst] (LDS DMA):
+    slice j = KK() rb + kk holds, at 16 lane bytes per lane, the operand registers of (rb,
+    kk) exactly as q_vloads would load them, so that one ds_read_b128 per slice brings them
+    back without bank conflicts."""
+    out = []
+    for rb in (0, 1):
+        for kk in range(KK()):
+            j = KK() * rb + kk
+            out.append(Ins("s_add_u32 m0, %%[qst], %d" % (1024 * j), "m0", defs=["m0"]))
+            out.append(Ins("s_mov_b32 %%[soff], %d" % (32 * ROWB() * rb + 32 * kk), "salu", defs=["%[soff]"]))
+            out.append(Ins("buffer_load_dwordx4 %[nqoff], %[nqrs], %[soff] offen lds", "dma", uses=["m0", "%[soff]"]))
+    return out
+
+
+def q_unstage():
+    """Q from the staging area at %[qlds] (this lane's 16 bytes of slice 0) into the operand
+    registers."""
+    out = []
+    for rb in (0, 1):
+        for kk in range(KK()):
+            j = KK() * rb + kk
+            out.append(Ins("ds_read_b128 %s, %%[qlds] offset:%d" % (vrange(Qr(rb, kk), 4), 1024 * j), "lds",
+                           defs=regs(Qr(rb, kk), 4)))
+            if j % 8 == 7:
+                out.append(Ins("s_waitcnt lgkmcnt(0)", "waitall"))
+    return out
+
+
+def kv_prefetch(g, nw):
+    """The next item's first tiles into the other LDS buffer set (%[nkdst]: its K buffer 0 plus
+    this wave's slice): K tile 0 to K buffer 0, K tile 1 (when the next item has one) to K
+    buffer 1, V tile 0 to V buffer 1, from the next head (%[nkrs], %[nvrs])."""
+    def tile(dst, rs):
+        out = []
+        for i in range(TILE() // 1024 // nw):
+            out.append(Ins("s_add_u32 m0, %%[nkdst], %d" % (dst + 1024 * nw * i), "m0", defs=["m0"]))
+            out.append(Ins("s_mov_b32 %%[soff], %d" % (src_of[dst] + 1024 * nw * i), "salu", defs=["%[soff]"]))
+            out.append(Ins("buffer_load_dwordx4 %%[dma%d], %s, %%[soff] offen lds" % (i & 1, rs), "dma",
+                           uses=["m0", "%[soff]"]))
+        return out
+    src_of = {0: 0, TILE(): TILE(), 3 * TILE(): 0}
+    out = tile(0, "%[nkrs]")
+    out.append(Cond(["s_cmp_gt_u32 %[nnt], 1"], tile(TILE(), "%[nkrs]"), "L_pk1_%d" % len(g.labels)))
+    g.labels.append(1)
+    out.extend(tile(3 * TILE(), "%[nvrs]"))
+    return out
+
+
+def prefetch(g, nw, with_q):
+    """The next item's loads, issued once per item by every wave in the same two steps: its
+    first K/V tiles when %[kit] reaches %[pkv], its Q rows when %[kit] reaches %[pq] (a step
+    no S product of this item follows; ~0 when there is no next item)."""
+    out = [Cond(["s_cmp_eq_u32 %[kit], %[pkv]"], kv_prefetch(g, nw), "L_pkv%d" % len(g.labels))]
+    g.labels.append(1)
+    if with_q:
+        out.append(Cond(["s_cmp_eq_u32 %[kit], %[pq]"], q_stage(), "L_pq%d" % len(g.labels)))
+        g.labels.append(1)
+    return out
+
+
 # ---------------------------------------------------------------- the program
 
 def half_groups(g, s_next, pv_prev):
@@ -828,12 +906,17 @@ def build(elem, causal, nw):
         prog.append(Ins("v_mov_b32 %s, %s" % (vr(Mr(rb)), NEG_INF_BITS), "valu", defs=[vr(Mr(rb))]))
         prog.append(Ins("v_mov_b32 %s, 0" % vr(Lr(rb)), "valu", defs=[vr(Lr(rb))]))
     prog.append(Ins("s_mov_b32 %[kit], 1", "salu", defs=["%[kit]"]))
-    prog.append(Ins("v_add_u32_e32 %s, 0x%x, %%[qoff]" % (vr(t(0)), 32 * ROWB()), "valu", defs=[vr(t(0))]))
-    for rb in all_rb:
-        for kk in range(KK()):
-            base = "%[qoff]" if rb == 0 else vr(t(0))
-            prog.append(Ins("buffer_load_dwordx4 %s, %s, %%[qrs], 0 offen offset:%d" % (vrange(Qr(rb, kk), 4), base, 32 * kk),
-                            "vload", defs=regs(Qr(rb, kk), 4), uses=[] if rb == 0 else [vr(t(0))]))
+    # ---- Q and the first tiles: K(0), K(1) (if any), V(0).  The first item of a workgroup
+    # loads them here (%[pf] = 0) and waits for them; a later one finds them prefetched by the
+    # item before it (its K/V in this item's buffer set, its Q staged in LDS), waits only for
+    # loads older than that item's epilogue stores, and reads Q back from the staging area.
+    own = q_vloads() + dma_tile("k", nw) + advance_k()
+    own.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k", nw), "L_k1"))
+    own.extend(advance_k() + dma_tile("v", nw) + advance_v())
+    staged = [Ins("s_waitcnt vmcnt(%d)" % nstores(), "wait")] + q_unstage()
+    staged.extend(advance_k() + advance_k() + advance_v())
+    prog.append(Cond(["s_cmp_eq_u32 %[pf], 0"], own, "L_own"))
+    prog.append(Cond(["s_cmp_lg_u32 %[pf], 0"], staged, "L_staged"))
     zero = list(range(32 * DB()))
     if MFMA_ROWSUM:
         zero += list(range(Lacc(0), Lacc(0) + 2 * LACC_REGS))
@@ -841,15 +924,11 @@ def build(elem, causal, nw):
         prog.append(Ins("v_accvgpr_write_b32 a%d, 0" % a, "accw", defs=["a%d" % a]))
     if MFMA_ROWSUM:
         prog.extend(ones16(elem))
-    # ---- first tiles: K(0), K(1) (if any), V(0), in flight together with the Q loads: the
-    # barrier's wait covers both
-    prog.extend(dma_tile("k", nw))
-    prog.extend(advance_k())
-    prog.append(Cond(["s_cmp_gt_u32 %[nt], 1"], dma_tile("k", nw), "L_k1"))
-    prog.extend(advance_k())
-    prog.extend(dma_tile("v", nw))
-    prog.extend(advance_v())
-    prog.extend(barrier())
+    prog.append(Cond(["s_cmp_eq_u32 %[pf], 0"], [Ins("s_waitcnt vmcnt(0)", "wait")], "L_ownw"))
+    # every wave's share of the first tiles has landed (the stores of the item before, at most
+    # nstores() younger vector memory operations, need not have)
+    prog.append(Ins("s_waitcnt vmcnt(%d) lgkmcnt(0)" % nstores(), "waitall"))
+    prog.append(Ins("s_barrier", "barrier"))
     for r in range(8 * KK()):
         prog.append(Ins("v_xor_b32_e32 v%d, %%[flip], v%d" % (r, r), "valu", defs=["v%d" % r], uses=["v%d" % r]))
     # S(0) alone
@@ -910,6 +989,7 @@ def build(elem, causal, nw):
     # iteration L: half 2L-1 unmasked, half 2L masked A
     head, dmas = iter_head(True, False)
     pathA.extend(head)
+    pathA.extend(prefetch(g, nw, False))
     pathA.extend(lim_ops("limA"))
     pathA.extend(half_interleaved(g, (0, 0, all_rb), (0, 0, all_rb),
                                   soft(g, 1, 1, 1, {}, False, ()), 0, dmas,
@@ -928,6 +1008,7 @@ def build(elem, causal, nw):
     tail = []
     head, dmas = iter_head(True, True)
     tail.extend(head)
+    tail.extend(prefetch(g, nw, True))
     tail.extend(lim_ops("limB"))
     tail.extend(half_interleaved(g, None, (0, 0, all_rb),
                                  soft(g, 1, 1, 1, maskB, False, deadB), 0, dmas,
@@ -940,12 +1021,16 @@ def build(elem, causal, nw):
     duty = []
     head, dmas = iter_head(True, True)
     duty.extend(head)
+    duty.extend(prefetch(g, nw, True))
     duty.extend(dmas)
     duty.append(Ins("s_add_u32 %[kit], %[kit], 1", "salu", defs=["%[kit]"], uses=["%[kit]"]))
     tail.append(Ins("s_sub_u32 %[cnt], %[nt], %[last]", "salu", defs=["%[cnt]"]))
     tail.append(Ins("s_sub_u32 %[cnt], %[cnt], 1", "salu", defs=["%[cnt]"]))
-    tail.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", duty, "L_duty")], "L_skipduty"))
-    tail.append(Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"))
+    # a wave that staged the next Q after its own stores waits for it here, so that the next
+    # item's wait for loads older than its last nstores() operations covers it
+    tail.append(Cond(["s_cmp_lg_u32 %[cnt], 0"], [Loop("%[cnt]", duty, "L_duty"), Ins("s_waitcnt vmcnt(0)", "wait")],
+                     "L_skipduty"))
+    tail.append(Ins("s_waitcnt lgkmcnt(0)", "wait"))
     return g, prog, pathA, pathB, tail
 
 

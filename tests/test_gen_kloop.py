@@ -38,7 +38,8 @@ def staging_events(gen, seq):
     for ins in seq:
         if ins.kind == "lds":
             for r in ins.defs:
-                ev.setdefault(r, []).append("W")
+                if lo <= int(r[1:]) < hi:        # Q read back from its LDS staging is no operand slot
+                    ev.setdefault(r, []).append("W")
         elif ins.kind == "mfma":
             for r in ins.uses:
                 if r.startswith("v") and lo <= int(r[1:]) < hi:
@@ -76,3 +77,44 @@ def test_the_checker_sees_a_read_that_runs_too_far_ahead(gen):
     doubled = [reg for reg, e in staging_events(gen, seq).items()
                if any(a == "W" and b == "W" for a, b in zip(e, e[1:]))]
     assert doubled
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_next_item_loads_are_older_than_the_stores_its_first_barrier_may_leave(gen, d, causal):
+    """An item's first barrier waits for vmcnt(n) with n = the epilogue's store count: the
+    item before loaded this item's Q (staged in LDS) and first tiles ahead of its epilogue, so
+    with vector memory completing in issue order those loads are done once at most n younger
+    operations remain.  That holds when the Q staging in the tail is followed by exactly the
+    epilogue's stores, and when a wave that stages Q later (in its duty steps, after its
+    stores) waits for everything before the item ends."""
+    gen.D = d
+    g, prog, path_a, path_b, tail = gen.build("bf16", causal, 4)
+    n = gen.nstores()
+    assert n == 2 + 8 * (d // 32)
+    conds = [k for k, it in enumerate(tail) if isinstance(it, gen.Cond) and any("%[pq]" in x for x in it.test)]
+    assert len(conds) == 1
+    rest = tail[conds[0] + 1:]
+    duty = [it for it in rest if isinstance(it, gen.Cond) and any(isinstance(b, gen.Loop) for b in it.body)]
+    assert len(duty) == 1
+    # the tail's own tile loads run only while %[kit] < %[nt], never in the step (%[kit] == %[nt])
+    # that stages Q
+    def at_last_step(items, out):
+        for it in items:
+            if isinstance(it, gen.Ins):
+                out.append(it)
+            elif not (isinstance(it, gen.Cond) and any(x.startswith("s_cmp_lt_u32") and "%[nt]" in x for x in it.test)):
+                at_last_step(it.body, out)
+        return out
+    straight = at_last_step([it for it in rest if it is not duty[0]], [])
+    assert sum(1 for ins in straight if ins.kind == "vstore") == n
+    assert not any(ins.kind in ("dma", "vload") for ins in straight)
+    assert duty[0].body[-1].text == "s_waitcnt vmcnt(0)"
+    loop = [b for b in duty[0].body if isinstance(b, gen.Loop)][0]
+    assert any(isinstance(it, gen.Cond) and any("%[pq]" in x for x in it.test) for it in loop.body)
+    # the first barrier: the item's own loads (first item) are waited for in full just before
+    seq = flatten(gen, prog, [])
+    k = next(i for i, ins in enumerate(seq) if ins.kind == "barrier")
+    assert seq[k - 1].text == "s_waitcnt vmcnt(%d) lgkmcnt(0)" % n
+    own = [it for it in prog if isinstance(it, gen.Cond) and it.test == ["s_cmp_eq_u32 %[pf], 0"]]
+    assert [b.text for b in own[-1].body] == ["s_waitcnt vmcnt(0)"]
