@@ -430,3 +430,32 @@ def test_many_heads_of_few_keys(fa, oracle, B, Hq, Hkv, N):
     ro, rl = oracle.attention(q, k, v, causal=True, scale=scale)
     check(o.numpy(), ro, "bf16", "O many heads")
     check(lse.numpy(), rl, "bf16", "LSE many heads")
+
+
+def walks(units, N, causal):
+    """Whether the library walks pairs of 256-row query tiles for this grid: the rule of
+    w64_walk_blocks (fa_fwd_w64.hip), written out here with this device's CU count."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nt = (N + 255) // 256
+    if units * nt <= cus:
+        return False
+    rounds = -(-(units * ((nt + 1) // 2)) // cus)
+    if causal:
+        walk, tiles = rounds * (nt + 1), max(units * nt * (nt + 1) / 2 / cus, nt)
+    else:
+        walk, tiles = 2 * rounds, -(-(units * nt) // cus)
+    return walk <= 1.03 * tiles
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dtype,causal", [
+    (2, 32, 32, 4000, 128, "bf16", True),      # last query tile 160 rows, its last key tile 32 keys
+    (1, 32, 8, 4050, 128, "f16", True),        # grouped K/V, 210-row last tile
+    (2, 32, 32, 3900, 64, "f16", True),
+    (4, 16, 16, 2000, 64, "bf16", False),      # every item the same length, 208-row last tile
+])
+def test_walked_grids_with_a_ragged_last_tile(fa, oracle, B, Hq, Hkv, N, d, dtype, causal):
+    """Grids large enough for the 256-row walk, where each item loads the next item's first
+    tiles and Q rows during its last steps, with N not a multiple of the tile: the items
+    differ in key-tile count, the last one holds rows past N.  Every row against the oracle."""
+    assert walks(B * Hq, N, causal)
+    parity(fa, oracle, B, Hq, Hkv, N, d, dtype, causal, seed=N + d)
