@@ -74,6 +74,9 @@ WORKLOADS = {
     "c2h_f16_n2048_d64": Workload("c2h_f16_n2048_d64", 4, 16, 16, 2048, 64, "f16", False, seed=1007),
     "c3h_f16_n4096_d128_causal": Workload("c3h_f16_n4096_d128_causal", 2, 32, 32, 4096, 128, "f16", True,
                                           seed=1008),
+    # fp32 inputs at the bench workload's shape (the fp32 contract config is too small to time)
+    "c3f_f32_n4096_d128_causal": Workload("c3f_f32_n4096_d128_causal", 2, 32, 32, 4096, 128, "f32", True,
+                                          seed=1009),
 }
 
 BENCH_WORKLOAD = "c3_bf16_n4096_d128_causal"
