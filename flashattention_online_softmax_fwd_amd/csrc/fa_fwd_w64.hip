@@ -167,7 +167,7 @@ fwd_w64_kernel(const FwdParams p)
     // A negative scale is folded into Q's sign; a zero scale becomes the smallest normal.
     const float c = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const unsigned flip = p.scale_log2 >= 0.f ? 0u : 0x80008000u;
-    // The item's rows, O rows and key tiles.
+    // Key tiles of 64 that query tile qt visits: up to the end of its last row when causal.
     auto key_tiles = [&](int qt) {
         const int kv_end = CAUSAL ? min(N, qt * BM + BM) : N;
         return (kv_end + 63) / 64;
@@ -178,142 +178,142 @@ fwd_w64_kernel(const FwdParams p)
     int qlds = 0;                    // then: this lane's 16 bytes of the staged Q
 #pragma nounroll
     while (j < jend) {
-    int bh, qt;
-    tile_of(j, s, bh, qt);
-    int jn = j, sn = s;
-    next_of(jn, sn);
-    const bool has_next = jn < jend;
-    int bhn = bh, qtn = qt;
-    if (has_next) tile_of(jn, sn, bhn, qtn);
+        int bh, qt;
+        tile_of(j, s, bh, qt);
+        int jn = j, sn = s;
+        next_of(jn, sn);
+        const bool has_next = jn < jend;
+        int bhn = bh, qtn = qt;
+        if (has_next) tile_of(jn, sn, bhn, qtn);
 
-    const int b = bh / p.Hq;
-    const int hk = (bh - b * p.Hq) / p.group;
-    const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
-    const char* Vh = (const char*)p.v + (size_t)(b * p.Hkv + hk) * N * ROWB;
-    const char* Qh = (const char*)p.q + (size_t)bh * N * ROWB;
-    char* Oh = (char*)p.o + (size_t)bh * N * ROWB;
-    float* Lh = p.lse + (size_t)bh * N;
-    const __amdgpu_buffer_rsrc_t krs = rsrc(Kh, range);
-    const __amdgpu_buffer_rsrc_t vrs = rsrc(Vh, range);
-    const __amdgpu_buffer_rsrc_t qrs = rsrc(Qh, range);
-    const __amdgpu_buffer_rsrc_t ors = rsrc(Oh, range);
-    const __amdgpu_buffer_rsrc_t lrs = rsrc(Lh, N * 4);
-    // the next item's head (its K/V tiles and Q rows are loaded in this item's last steps)
-    const int bn = bhn / p.Hq;
-    const int hkn = (bhn - bn * p.Hq) / p.group;
-    const __amdgpu_buffer_rsrc_t nkrs = rsrc((const char*)p.k + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
-    const __amdgpu_buffer_rsrc_t nvrs = rsrc((const char*)p.v + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
-    const __amdgpu_buffer_rsrc_t nqrs = rsrc((const char*)p.q + (size_t)bhn * N * ROWB, range);
+        const int b = bh / p.Hq;
+        const int hk = (bh - b * p.Hq) / p.group;
+        const char* Kh = (const char*)p.k + (size_t)(b * p.Hkv + hk) * N * ROWB;
+        const char* Vh = (const char*)p.v + (size_t)(b * p.Hkv + hk) * N * ROWB;
+        const char* Qh = (const char*)p.q + (size_t)bh * N * ROWB;
+        char* Oh = (char*)p.o + (size_t)bh * N * ROWB;
+        float* Lh = p.lse + (size_t)bh * N;
+        const __amdgpu_buffer_rsrc_t krs = rsrc(Kh, range);
+        const __amdgpu_buffer_rsrc_t vrs = rsrc(Vh, range);
+        const __amdgpu_buffer_rsrc_t qrs = rsrc(Qh, range);
+        const __amdgpu_buffer_rsrc_t ors = rsrc(Oh, range);
+        const __amdgpu_buffer_rsrc_t lrs = rsrc(Lh, N * 4);
+        // the next item's head (its K/V tiles and Q rows are loaded in this item's last steps)
+        const int bn = bhn / p.Hq;
+        const int hkn = (bhn - bn * p.Hq) / p.group;
+        const __amdgpu_buffer_rsrc_t nkrs = rsrc((const char*)p.k + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
+        const __amdgpu_buffer_rsrc_t nvrs = rsrc((const char*)p.v + (size_t)(bn * p.Hkv + hkn) * N * ROWB, range);
+        const __amdgpu_buffer_rsrc_t nqrs = rsrc((const char*)p.q + (size_t)bhn * N * ROWB, range);
 
-    const int q0 = qt * BM;
-    const int row0 = q0 + R * wave;                     // the wave's first query row
-    const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
-    const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
-    const int loff = (row0 + l32) * 4;
-    const int nqoff = (qtn * BM + R * wave + l32) * ROWB + 16 * hi;
-    const unsigned setb = ldsb + (unsigned)(set * 4 * TILE);
-    const unsigned nsetb = ldsb + (unsigned)((set ^ (SETS - 1)) * 4 * TILE);
+        const int q0 = qt * BM;
+        const int row0 = q0 + R * wave;                     // the wave's first query row
+        const int qoff = (row0 + l32) * ROWB + 16 * hi;      // Q: dims 16kk + 8hi .. of this lane's row
+        const int ooff = (row0 + l32) * ROWB + 8 * hi;       // O: dims 32db + 8g + 4hi .. of this lane's row
+        const int loff = (row0 + l32) * 4;
+        const int nqoff = (qtn * BM + R * wave + l32) * ROWB + 16 * hi;
+        const unsigned setb = ldsb + (unsigned)(set * 4 * TILE);
+        const unsigned nsetb = ldsb + (unsigned)((set ^ (SETS - 1)) * 4 * TILE);
 
-    // K operand: row l32 of the 32-key block, logical chunk 2kk + hi (buffer K0 to start).
-    const int kx = swz<D>(l32);
-    int koff[8] = {};
+        // K operand: row l32 of the 32-key block, logical chunk 2kk + hi (buffer K0 to start).
+        const int kx = swz<D>(l32);
+        int koff[8] = {};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)setb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
-    // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
-    // step and dims 32dt + 16(G&1) + 4s ..; buffer V0 to start (V tile 0 lands in V1).
-    const int G = lane >> 4;
-    const int jj = (lane >> 2) & 3;
-    const int ss = lane & 3;
-    int voff[8] = {};
+        for (int kk = 0; kk < D / 16; ++kk) koff[kk] = (int)setb + l32 * ROWB + 16 * ((2 * kk + hi) ^ kx);
+        // V operand (transposed reads): lane (group G, 4j + s) reads row 8r + 4(G>>1) + j of a 16-key
+        // step and dims 32dt + 16(G&1) + 4s ..; buffer V0 to start (V tile 0 lands in V1).
+        const int G = lane >> 4;
+        const int jj = (lane >> 2) & 3;
+        const int ss = lane & 3;
+        int voff[8] = {};
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int row = 8 * r + 4 * (G >> 1) + jj;
-        const int w = swz<D>(row);
+        for (int r = 0; r < 2; ++r) {
+            const int row = 8 * r + 4 * (G >> 1) + jj;
+            const int w = swz<D>(row);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
-            voff[(D / 32) * r + dt] = (int)setb + 2 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int chunk = 4 * dt + 2 * (G & 1) + (ss >> 1);
+                voff[(D / 32) * r + dt] = (int)setb + 2 * TILE + row * ROWB + 16 * (chunk ^ w) + 8 * (ss & 1);
+            }
         }
-    }
 
-    // Key tiles of 64 for the workgroup; the last one this wave's rows need.
-    const int nt = key_tiles(qt);
-    const int last = CAUSAL ? min(nt - 1, (q0 + R * wave) / 64) : nt - 1;
-    const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
-    const int limA = valid_last - 1;
-    const int limB = valid_last - 33;
-    const int nnt = key_tiles(qtn);
-    // The next item's loads: its first K/V tiles at step max(nt - 1, 1) into the other set, its
-    // Q rows at step nt (no S product of this item follows) into this wave's staging area: the
-    // K buffers and the idle V buffer of this set (waves 0-2) or V0 of the other set (wave 3),
-    // none of which this item reads after step nt - 1 or the next one fills before its own Q is read.
-    const unsigned never = 0xffffffffu;
-    const unsigned pkv = has_next ? (unsigned)max(nt - 1, 1) : never;
-    const unsigned pq = has_next ? (unsigned)nt : never;
-    const unsigned nkdst = nsetb + 1024 * wave;
-    unsigned qst;
-    if (wave == 0) qst = setb;
-    else if (wave == 1) qst = setb + TILE;
-    else if (wave == 2) qst = setb + 2 * TILE + ((nt + 1) & 1) * TILE;
-    else qst = nsetb + 2 * TILE;
-    const int qlds_next = (int)qst + 16 * lane;
+        // Key tiles of 64 for the workgroup; the last one this wave's rows need.
+        const int nt = key_tiles(qt);
+        const int last = CAUSAL ? min(nt - 1, (q0 + R * wave) / 64) : nt - 1;
+        const int valid_last = N - 64 * (nt - 1);            // keys of the last tile below N (non-causal mask)
+        const int limA = valid_last - 1;
+        const int limB = valid_last - 33;
+        const int nnt = key_tiles(qtn);
+        // The next item's loads: its first K/V tiles at step max(nt - 1, 1) into the other set, its
+        // Q rows at step nt (no S product of this item follows) into this wave's staging area: the
+        // K buffers and the idle V buffer of this set (waves 0-2) or V0 of the other set (wave 3),
+        // none of which this item reads after step nt - 1 or the next one fills before its own Q is read.
+        const unsigned never = 0xffffffffu;
+        const unsigned pkv = has_next ? (unsigned)max(nt - 1, 1) : never;
+        const unsigned pq = has_next ? (unsigned)nt : never;
+        const unsigned nkdst = nsetb + 1024 * wave;
+        unsigned qst;
+        if (wave == 0) qst = setb;
+        else if (wave == 1) qst = setb + TILE;
+        else if (wave == 2) qst = setb + 2 * TILE + ((nt + 1) & 1) * TILE;
+        else qst = nsetb + 2 * TILE;
+        const int qlds_next = (int)qst + 16 * lane;
 
-    // K tile j lands in K buffer j % 2, V tile j in V buffer (j + 1) % 2; the operand reads
-    // start at buffer 0 of each and flip before every tile (V tile j is read one tile later)
-    unsigned ksrc = 0, kdst = setb + 1024 * wave, vsrc = 0, vdst = setb + 3 * TILE + 1024 * wave;
-    unsigned soff, kit, cnt;
-    unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
-    int dlim;
+        // K tile j lands in K buffer j % 2, V tile j in V buffer (j + 1) % 2; the operand reads
+        // start at buffer 0 of each and flip before every tile (V tile j is read one tile later)
+        unsigned ksrc = 0, kdst = setb + 1024 * wave, vsrc = 0, vdst = setb + 3 * TILE + 1024 * wave;
+        unsigned soff, kit, cnt;
+        unsigned long long g00, g01, g10, g11, ga0, ga1, mk1, mk2, mk3, mk4, mk5, mk6, mk7;
+        int dlim;
 #define FA_W64_ASM_C(TEXT, CLOBBERS)                                                                       \
-    asm volatile(TEXT                                                                                      \
-                 : [koff0] "+v"(koff[0]), [koff1] "+v"(koff[1]), [koff2] "+v"(koff[2]), [koff3] "+v"(koff[3]),  \
-                   [koff4] "+v"(koff[4]), [koff5] "+v"(koff[5]), [koff6] "+v"(koff[6]), [koff7] "+v"(koff[7]),  \
-                   [voff0] "+v"(voff[0]), [voff1] "+v"(voff[1]), [voff2] "+v"(voff[2]), [voff3] "+v"(voff[3]),  \
-                   [voff4] "+v"(voff[4]), [voff5] "+v"(voff[5]), [voff6] "+v"(voff[6]), [voff7] "+v"(voff[7]),  \
-                   [ksrc] "+s"(ksrc), [kdst] "+s"(kdst), [vsrc] "+s"(vsrc), [vdst] "+s"(vdst),                   \
-                   [soff] "=&s"(soff), [kit] "=&s"(kit), [cnt] "=&s"(cnt),                                      \
-                   [g00] "=&s"(g00), [g01] "=&s"(g01), [g10] "=&s"(g10), [g11] "=&s"(g11), [ga0] "=&s"(ga0),    \
-                   [ga1] "=&s"(ga1), [mk1] "=&s"(mk1), [mk2] "=&s"(mk2), [mk3] "=&s"(mk3), [mk4] "=&s"(mk4),    \
-                   [mk5] "=&s"(mk5), [mk6] "=&s"(mk6), [mk7] "=&s"(mk7), [dlim] "=&v"(dlim)                     \
-                 : [dma0] "v"(dma[0]), [dma1] "v"(dma[1]), [qoff] "v"(qoff), [ooff] "v"(ooff), [loff] "v"(loff),  \
-                   [dmask] "v"(dmask), [hi4] "v"(hi4), [krs] "s"(krs), [vrs] "s"(vrs), [qrs] "s"(qrs),             \
-                   [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
-                   [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip), [pf] "s"(pf), [qlds] "v"(qlds),               \
-                   [pkv] "s"(pkv), [pq] "s"(pq), [nkrs] "s"(nkrs), [nvrs] "s"(nvrs), [nqrs] "s"(nqrs),            \
-                   [nqoff] "v"(nqoff), [nkdst] "s"(nkdst), [nnt] "s"(nnt), [qst] "s"(qst)                        \
-                 : CLOBBERS)
+        asm volatile(TEXT                                                                                      \
+                     : [koff0] "+v"(koff[0]), [koff1] "+v"(koff[1]), [koff2] "+v"(koff[2]), [koff3] "+v"(koff[3]),  \
+                       [koff4] "+v"(koff[4]), [koff5] "+v"(koff[5]), [koff6] "+v"(koff[6]), [koff7] "+v"(koff[7]),  \
+                       [voff0] "+v"(voff[0]), [voff1] "+v"(voff[1]), [voff2] "+v"(voff[2]), [voff3] "+v"(voff[3]),  \
+                       [voff4] "+v"(voff[4]), [voff5] "+v"(voff[5]), [voff6] "+v"(voff[6]), [voff7] "+v"(voff[7]),  \
+                       [ksrc] "+s"(ksrc), [kdst] "+s"(kdst), [vsrc] "+s"(vsrc), [vdst] "+s"(vdst),                   \
+                       [soff] "=&s"(soff), [kit] "=&s"(kit), [cnt] "=&s"(cnt),                                      \
+                       [g00] "=&s"(g00), [g01] "=&s"(g01), [g10] "=&s"(g10), [g11] "=&s"(g11), [ga0] "=&s"(ga0),    \
+                       [ga1] "=&s"(ga1), [mk1] "=&s"(mk1), [mk2] "=&s"(mk2), [mk3] "=&s"(mk3), [mk4] "=&s"(mk4),    \
+                       [mk5] "=&s"(mk5), [mk6] "=&s"(mk6), [mk7] "=&s"(mk7), [dlim] "=&v"(dlim)                     \
+                     : [dma0] "v"(dma[0]), [dma1] "v"(dma[1]), [qoff] "v"(qoff), [ooff] "v"(ooff), [loff] "v"(loff),  \
+                       [dmask] "v"(dmask), [hi4] "v"(hi4), [krs] "s"(krs), [vrs] "s"(vrs), [qrs] "s"(qrs),             \
+                       [ors] "s"(ors), [lrs] "s"(lrs), [nt] "s"(nt), [last] "s"(last), [limA] "s"(limA),              \
+                       [limB] "s"(limB), [c] "s"(c), [flip] "s"(flip), [pf] "s"(pf), [qlds] "v"(qlds),               \
+                       [pkv] "s"(pkv), [pq] "s"(pq), [nkrs] "s"(nkrs), [nvrs] "s"(nvrs), [nqrs] "s"(nqrs),            \
+                       [nqoff] "v"(nqoff), [nkdst] "s"(nkdst), [nnt] "s"(nnt), [qst] "s"(qst)                        \
+                     : CLOBBERS)
 #define FA_W64_ASM(TEXT) FA_W64_ASM_C(TEXT, FA_W64_CLOBBERS)
 #define FA_W64_PICK(W, DD)                                                                 \
-    if constexpr (__is_same(E, __bf16)) {                                                 \
-        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W##W##_D##DD);              \
-        else FA_W64_ASM(FA_KLOOP_BF16_FULL_W##W##_D##DD);                                 \
-    } else {                                                                              \
-        if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W##W##_D##DD);               \
-        else FA_W64_ASM(FA_KLOOP_F16_FULL_W##W##_D##DD);                                  \
-    }
-    if constexpr (D == 128) {
-        if constexpr (NW == 2) {
-            FA_W64_PICK(2, 128)
-        } else {
-            FA_W64_PICK(4, 128)
+        if constexpr (__is_same(E, __bf16)) {                                                 \
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_BF16_CAUSAL_W##W##_D##DD);              \
+            else FA_W64_ASM(FA_KLOOP_BF16_FULL_W##W##_D##DD);                                 \
+        } else {                                                                              \
+            if constexpr (CAUSAL) FA_W64_ASM(FA_KLOOP_F16_CAUSAL_W##W##_D##DD);               \
+            else FA_W64_ASM(FA_KLOOP_F16_FULL_W##W##_D##DD);                                  \
         }
-    } else {
-        if constexpr (NW == 2) {
-            FA_W64_PICK(2, 64)
+        if constexpr (D == 128) {
+            if constexpr (NW == 2) {
+                FA_W64_PICK(2, 128)
+            } else {
+                FA_W64_PICK(4, 128)
+            }
         } else {
-            FA_W64_PICK(4, 64)
+            if constexpr (NW == 2) {
+                FA_W64_PICK(2, 64)
+            } else {
+                FA_W64_PICK(4, 64)
+            }
         }
-    }
 #undef FA_W64_PICK
 #undef FA_W64_ASM
 #undef FA_W64_ASM_C
-    // No barrier here: the next item's first barrier comes before anything it writes to LDS
-    // could reach a tile this item still reads.
-    j = jn;
-    s = sn;
-    set ^= SETS - 1;
-    pf = 1;
-    qlds = qlds_next;
+        // No barrier here: the next item's first barrier comes before anything it writes to LDS
+        // could reach a tile this item still reads.
+        j = jn;
+        s = sn;
+        set ^= SETS - 1;
+        pf = 1;
+        qlds = qlds_next;
     }
 
     if (p.stamps && lane == 0) {
