@@ -363,6 +363,48 @@ def test_scale_one_overflow_stress(fa, oracle):
     check(lse.numpy(), rl, "bf16", "LSE scale-1 stress")
 
 
+def test_longest_head_the_abi_accepts(fa, oracle):
+    """The square causal forward on the longest head the ABI takes at d = 128 in bf16: (N + 128)
+    d 2 bytes just below 2^31, one head, the default kernel and grid walk.  Buffer ranges and
+    offsets are then the largest a launch can use; the last query tile holds 127 rows and the
+    last key tile 63 keys.  Twelve rows are compared with the oracle: both ends, the middle, and
+    rows of the last two query tiles (the diagonal key tile among them).  Those rows share one
+    query vector u, and four keys score 16 to 17.5 against it (about N(0, 1) for the 8.4M others)
+    with distinct value rows: the first key, the middle one, one in the second-to-last key tile
+    and the very last, so a tile mis-addressed near the end of the head moves O far past the bar.
+    One row more is refused before anything is launched.  (At d = 64 the longest head is twice as
+    long and four times the work, so d = 128 stands for both.)"""
+    d = 128
+    n = 0x7FFFFFFF // (2 * d) - 128
+    print("longest accepted head: N", n, flush=True)
+    q, k, v = fin.make_qkv_device(1, 1, 1, n, n, d, "bf16", seed=1401)
+    scale = 1.0 / math.sqrt(d)
+    rows = np.array([0, 1, 4096, n // 2, n // 2 + 1, n - 300, n - 128, n - 127, n - 66, n - 65, n - 2, n - 1])
+    u = q[0, 0, 0].clone()
+    q[0, 0, torch.from_numpy(rows).to(q.device)] = u
+    uf = u.float()
+    spikes = [(0, 16.0), (n // 2, 16.5), (n - 65, 17.0), (n - 1, 17.5)]
+    for i, (pos, target) in enumerate(spikes):
+        k[0, 0, pos] = (uf * (target / (scale * float(uf @ uf)))).to(torch.bfloat16)
+        row = torch.zeros(d, device=v.device)
+        row[8 * i + 3] = 8.0
+        v[0, 0, pos] = row.to(torch.bfloat16)
+    o, lse = fa.forward(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(q.device)
+    o_rows = o[0, 0, idx].float().cpu().numpy()
+    lse_rows = lse[0, 0, idx].cpu().numpy()
+    ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True, scale=scale, rows=rows)
+    for i, (pos, _) in enumerate(spikes):      # every planted key a row sees carries a visible share
+        seen = rows >= pos
+        assert np.all(ro[seen, 8 * i + 3] > 0.2), (i, ro[seen, 8 * i + 3])
+    check(o_rows, ro, "bf16", "O at the longest head")
+    check(lse_rows, rl, "bf16", "LSE at the longest head")
+    rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   1, 1, 1, n + 1, d, 1, scale, fa.FA_DTYPE_BF16, None)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "2 GiB" in fa.fa_last_error()
+
+
 def test_empty_problem_enqueues_nothing(fa):
     q = torch.zeros(0, 2, 16, 64, device="cuda", dtype=torch.bfloat16)
     o, lse = fa.forward(q, q, q)
