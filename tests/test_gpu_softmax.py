@@ -108,6 +108,40 @@ def test_in_place_and_deterministic(fa, algo):
     assert torch.equal(y, y2) and torch.equal(lse, lse2) and torch.equal(xi, y)
 
 
+def test_longest_row_the_abi_accepts(fa, oracle):
+    """One fp32 row of 2^31 - 4096 entries (8 GiB), the most columns the ABI takes: the element
+    index, and the unrolled loop's last step past it, stay below 2^31 while the row's byte
+    offsets pass 2^32.  Standard normals times 4 with three planted entries, 50 near the start,
+    55 in the middle and 60 at the very end, so the online pass moves its maximum twice and
+    last at the final entry.  Both algorithms: the LSE and the outputs at both ends, at the
+    planted entries and at 4096 seeded positions against the oracle, the sum of the row near 1,
+    and one column more refused before anything is launched."""
+    cols = 0x7FFFFFFF - 4095
+    print("longest accepted row: cols", cols, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1501)
+    x = torch.randn((1, cols), generator=g, device="cuda", dtype=torch.float32) * 4.0
+    planted = [3, cols // 2, cols - 1]
+    for j, val in zip(planted, (50.0, 55.0, 60.0)):
+        x[0, j] = val
+    idx = np.unique(np.concatenate([[0, 1, cols - 2], planted,
+                                    np.random.default_rng(1501).choice(cols, 4096, replace=False)]))
+    ry, rl = oracle.softmax_rows(x.cpu())
+    ry = ry[:, idx]
+    for algo in ("online", "safe"):
+        y, lse = fa.softmax(x, algo=algo)
+        torch.cuda.synchronize()
+        total = float(torch.sum(y, dtype=torch.float64))
+        yr = y[:, torch.as_tensor(idx, device=y.device)].cpu().numpy()
+        lr = lse.cpu().numpy()
+        del y
+        check(yr, lr, ry, rl, "f32", "longest row " + algo)
+        assert abs(total - 1.0) < 1e-3, (algo, total)
+    assert ry[0, np.searchsorted(idx, cols - 1)] > 0.99
+    rc = fa.fa_softmax(x.data_ptr(), x.data_ptr(), None, 1, cols + 1, fa.FA_DTYPE_F32, fa.FA_SOFTMAX_ONLINE, None)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "columns" in fa.fa_last_error()
+
+
 @pytest.mark.parametrize("algo", ["online", "safe"])
 @pytest.mark.parametrize("name", sorted(fin.SOFTMAX_WORKLOADS))
 def test_measured_workloads_at_full_size(fa, oracle, name, algo):
