@@ -24,6 +24,13 @@ constexpr int kMaxSplits = 1024;
 constexpr int kMaxBwdSplits = 8;
 constexpr uint64_t kTileSlack = 128;   // rows a kernel may address past N in its last tile
 constexpr int kMaxSoftmaxCols = 0x7fffffff - 4095;   // 2^31 - 4096
+// A launch's work-item count (workgroups x threads) is a 32-bit quantity, and every kernel here
+// runs at most 256 threads per workgroup: at most this many workgroups per launch.
+constexpr uint64_t kMaxWorkgroups = 0xffffffffULL / 256;   // 2^24 - 1
+// The row softmax runs one workgroup per row and launches longer lists in pieces of this many rows.
+constexpr long long kSoftmaxRowsPerLaunch = 1LL << 23;
+// The merge runs four rows per workgroup in a single launch.
+constexpr uint64_t kMaxMergeRows = 4 * kMaxWorkgroups;
 
 int fail(int code, const std::string& msg)
 {
@@ -177,7 +184,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     }
     const uint64_t ntiles = ((uint64_t)N + e->block_m - 1) / e->block_m;
     uint64_t grid = (uint64_t)B * (uint64_t)Hq * ntiles;
-    if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if (grid > kMaxWorkgroups) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^24 - 1 workgroups");
     if (e->blocks) {
         const long long walk = e->blocks((long long)B * Hq, (long long)ntiles, causal);
         if (walk > 0) grid = (uint64_t)walk;
@@ -269,7 +276,7 @@ int run_splitkv(const void* q, const void* k, const void* v, float* o_part, floa
         return fail(FA_ERR_UNSUPPORTED, "more than 2^31 - 129 query rows per K/V head (G * Nq)");
     const uint64_t ntiles = (packed + e->block_m - 1) / e->block_m;
     const uint64_t grid = (uint64_t)num_splits * (uint64_t)B * (uint64_t)Hkv * ntiles;
-    if (grid > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if (grid > kMaxWorkgroups) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^24 - 1 workgroups");
 
     fa::FwdParams p;
     p.q = q;
@@ -319,7 +326,8 @@ int run_merge(const float* o_part, const float* lse_part, void* o, float* lse, i
         overlaps(lse, lbytes, o_part, pbytes) || overlaps(lse, lbytes, lse_part, plbytes) ||
         overlaps(o, obytes, lse, lbytes))
         return fail(FA_ERR_INVALID_ARG, "o and lse must not overlap the partial states or each other");
-    if ((rows + 3) / 4 > 0x7fffffffULL) return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if (rows > kMaxMergeRows)
+        return fail(FA_ERR_UNSUPPORTED, "more than " + std::to_string(kMaxMergeRows) + " rows (B * H * N) in one merge");
 
     fa::MergeParams p;
     p.o_part = o_part;
@@ -355,16 +363,21 @@ int run_softmax(const void* x, void* y, float* lse, long long rows, int cols, in
         return fail(FA_ERR_INVALID_ARG, "y must be x itself or not overlap it");
     if (lse && (overlaps(lse, (uint64_t)rows * 4, x, bytes) || overlaps(lse, (uint64_t)rows * 4, y, bytes)))
         return fail(FA_ERR_INVALID_ARG, "lse must not overlap x or y");
+    // One workgroup per row, so a long list of rows goes out in launches of at most
+    // kSoftmaxRowsPerLaunch rows (2^23: each piece starts 16-byte aligned like x itself).
+    const uint64_t row_bytes = (uint64_t)cols * (dtype == FA_DTYPE_F32 ? 4 : 2);
     fa::SoftmaxParams p;
-    p.x = x;
-    p.y = y;
-    p.lse = lse;
-    p.rows = rows;
     p.cols = cols;
     p.dtype = dtype;
     p.online = algo == FA_SOFTMAX_ONLINE;
-    const hipError_t err = fa::launch_softmax(p, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    for (long long r0 = 0; r0 < rows; r0 += kSoftmaxRowsPerLaunch) {
+        p.x = static_cast<const char*>(x) + (uint64_t)r0 * row_bytes;
+        p.y = static_cast<char*>(y) + (uint64_t)r0 * row_bytes;
+        p.lse = lse ? lse + r0 : nullptr;
+        p.rows = std::min(rows - r0, kSoftmaxRowsPerLaunch);
+        const hipError_t err = fa::launch_softmax(p, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return fail(FA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+    }
     return FA_OK;
 }
 
@@ -414,10 +427,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     }
     // one workgroup per 128 query rows (dq), per 128 keys and split (dk, dv), per 8 elements (reduce)
     const uint64_t tiles = ((uint64_t)N + 127) / 128;
-    if ((uint64_t)B * (uint64_t)Hq * tiles > 0x7fffffffULL ||
-        (uint64_t)B * (uint64_t)Hkv * tiles * (uint64_t)num_splits > 0x7fffffffULL ||
-        (2 * kvelems / 8 + 255) / 256 > 0x7fffffffULL)
-        return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^31 - 1 workgroups");
+    if ((uint64_t)B * (uint64_t)Hq * tiles > kMaxWorkgroups ||
+        (uint64_t)B * (uint64_t)Hkv * tiles * (uint64_t)num_splits > kMaxWorkgroups ||
+        (2 * kvelems / 8 + 255) / 256 > kMaxWorkgroups)
+        return fail(FA_ERR_UNSUPPORTED, "grid exceeds 2^24 - 1 workgroups");
 
     fa::BwdParams p;
     p.q = q;

@@ -111,7 +111,7 @@ struct SoftmaxParams {
     const void* x;
     void* y;
     float* lse;        // may be null
-    long long rows;    // <= 2^31 - 1 (one workgroup per row)
+    long long rows;    // rows of this launch, <= 2^23 (one workgroup per row)
     int cols;
     int dtype;         // FA_DTYPE_*: x and y
     bool online;       // true: running max and sum in one pass; false: three passes

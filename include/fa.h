@@ -198,7 +198,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o_part, f
  *   per row:  m = max_s lse_s,  w_s = exp(lse_s - m),  lse = m + ln sum_s w_s,
  *             o = sum_s w_s o_s / sum_s w_s; a row whose states are all empty
  *             gets o = 0 and lse = -inf
- *   d         64 or 128; B, N >= 0 (0: FA_OK, nothing touched); H >= 1
+ *   d         64 or 128; B, N >= 0 (0: FA_OK, nothing touched); H >= 1;
+ *             B * H * N <= 67108860 rows (one launch of four rows per workgroup
+ *             within 2^32 work-items; FA_ERR_UNSUPPORTED beyond)
  * Any set of states of disjoint key sets in this form may be merged, e.g. the
  * outputs of fa_fwd_splitkv over different K/V shards.  Ownership, alignment,
  * overlap and error rules as for fa_fwd.

@@ -208,6 +208,16 @@ def test_merge_rejects_bad_arguments(lib, args, code):
     assert lib.fa_last_error() != b""
 
 
+def test_merge_row_limit(lib):
+    """One merge launch runs four rows per 256-thread workgroup, and a launch's work-item count
+    is 32-bit: more than 4 * (2^24 - 1) rows are refused before any HIP call (only the refused
+    side is called here: the accepted side would launch)."""
+    rows = 4 * (0xFFFFFFFF // 256) + 1
+    # far-apart pointers, so the huge extents do not overlap
+    assert lib.fa_merge(1 << 40, 2 << 40, 3 << 40, 4 << 40, 1, 1, 1, rows, 64, 1, None) == 2
+    assert b"rows" in lib.fa_last_error()
+
+
 def test_split_chunk_and_default_splits(lib):
     assert lib.fa_split_chunk(4096, 1) == 4096
     assert lib.fa_split_chunk(4096, 3) == 1408          # ceil(4096/3) = 1366 -> next multiple of 64

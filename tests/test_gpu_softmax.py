@@ -108,6 +108,27 @@ def test_in_place_and_deterministic(fa, algo):
     assert torch.equal(y, y2) and torch.equal(lse, lse2) and torch.equal(xi, y)
 
 
+@pytest.mark.parametrize("cols", [3, 4])
+def test_more_rows_than_one_launch_holds(fa, oracle, cols):
+    """2^24 + 3 rows: one workgroup per row, so the library launches them in pieces of 2^23 rows
+    (a single launch of them would pass the 32-bit work-item count).  Rows on both sides of each
+    piece boundary, the last row and a seeded sample against the oracle; every row sums to 1.
+    Three columns take the scalar path (rows 12 bytes apart), four the 16-byte vector path."""
+    rows = (1 << 24) + 3
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1502 + cols)
+    x = torch.randn((rows, cols), generator=g, device="cuda", dtype=torch.float32) * 4.0
+    edges = [0, (1 << 23) - 1, 1 << 23, (1 << 24) - 1, 1 << 24, rows - 1]
+    pick = np.unique(np.concatenate([edges, np.random.default_rng(1502).choice(rows, 2000, replace=False)]))
+    ry, rl = oracle.softmax_rows(x[torch.as_tensor(pick, device=x.device)].cpu())
+    for algo in ("online", "safe"):
+        y, lse = fa.softmax(x, algo=algo)
+        torch.cuda.synchronize()
+        sel = torch.as_tensor(pick, device=y.device)
+        check(y[sel].cpu().numpy(), lse[sel].cpu().numpy(), ry, rl, "f32", "%d rows x %d %s" % (rows, cols, algo))
+        assert torch.all(torch.abs(y.double().sum(dim=1) - 1) < 1e-5).item()
+
+
 def test_longest_row_the_abi_accepts(fa, oracle):
     """One fp32 row of 2^31 - 4096 entries (8 GiB), the most columns the ABI takes: the element
     index, and the unrolled loop's last step past it, stay below 2^31 while the row's byte
