@@ -271,6 +271,10 @@ def cpu_baseline(w, q, k, v, o, lse, budget_s):
                   % (len(rows), w.name, flops, w.flops, spent),
         "seconds": spent,
         "rows": int(len(rows)),
+        # the whole workload on the oracle: measured when the sample is every row, else the
+        # sample's time scaled by the workload's flops over the sample's
+        "full_problem_seconds": spent * w.flops / flops,
+        "full_problem_seconds_kind": "measured" if len(rows) == total else "extrapolated",
         "gpu_matches_oracle_on_sample": ok,
         "max_abs_err_o": float(np.abs(go - ro).max()),
         "max_abs_err_lse": float(np.abs(gl - rl).max()),

@@ -104,3 +104,22 @@ def test_bench_names_the_kernel_the_library_dispatches():
             nw, rows = 4, 128
         want = units * ((w.N + rows - 1) // rows) * nw
         assert lib.fa_fwd_stamp_slots(w.B, w.Hq, w.N, w.d, code) == want, (name, src, kname)
+
+
+def test_cpu_baseline_reports_the_whole_workload_time():
+    """cpu_baseline's full_problem_seconds: the measured time when every row was done, else the
+    sample's time scaled by the workload's flops over the sample's, labelled extrapolated.  Run
+    on the CPU with the oracle's own outputs standing in for the GPU's."""
+    import torch
+    from oracle import fa_oracle
+    w = fin.WORKLOADS["c1_f32_n256_d64"]
+    q, k, v = fin.workload_inputs(w)
+    ro, rl = fa_oracle.attention(q, k, v, causal=w.causal, scale=w.softmax_scale)
+    o, lse = torch.from_numpy(ro).float(), torch.from_numpy(rl).float()
+    full = bench.cpu_baseline(w, q, k, v, o, lse, 60.0)
+    assert full["rows"] == 256 and full["full_problem_seconds_kind"] == "measured"
+    assert full["full_problem_seconds"] == pytest.approx(full["seconds"])
+    part = bench.cpu_baseline(w, q, k, v, o, lse, 1e-12)      # stops after its first chunk of 64 rows
+    assert part["rows"] == 64 and part["full_problem_seconds_kind"] == "extrapolated"
+    assert part["gpu_matches_oracle_on_sample"]
+    assert part["full_problem_seconds"] > part["seconds"]
