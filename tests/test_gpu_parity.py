@@ -405,6 +405,30 @@ def test_longest_head_the_abi_accepts(fa, oracle):
     assert rc == fa.FA_ERR_UNSUPPORTED and "2 GiB" in fa.fa_last_error()
 
 
+def test_no_device_memory_beyond_the_outputs(fa):
+    """The method never holds a row of scores (spicyshark.co lesson: its opening prices the score
+    table of 32,768 tokens at 4 GiB per head, and the last check of "Proof it works" catches a
+    streaming version that quietly builds every score).  A causal forward over 8 heads of 32768
+    keys, whose fp32 score table would take 34 GB, with O and LSE given: after one warm-up call
+    (which loads the code objects), three more calls leave torch's allocator untouched and the
+    device's free memory (hipMemGetInfo) unchanged within 64 MiB."""
+    n = 32768
+    q, k, v = fin.make_qkv_device(1, 8, 8, n, n, 128, "bf16", seed=1701)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 8, n), dtype=torch.float32, device=q.device)
+    fa.forward(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0, reserved0 = torch.cuda.memory_allocated(), torch.cuda.memory_reserved()
+    for _ in range(3):
+        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == alloc0 and torch.cuda.memory_reserved() == reserved0
+    assert abs(free0 - free1) < 64 << 20, (free0, free1)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
 def test_empty_problem_enqueues_nothing(fa):
     q = torch.zeros(0, 2, 16, 64, device="cuda", dtype=torch.bfloat16)
     o, lse = fa.forward(q, q, q)
