@@ -1127,10 +1127,6 @@ def assemble(elem, causal, nw, d=128):
     return out
 
 
-def c_string(lines):
-    return "\n".join('    "%s\\n"' % l.replace('"', '\\"') for l in lines)
-
-
 def main():
     parts = ["// Generated by gen_fwd_kloop.py; do not edit.  The key loop of the 64-rows-per-wave\n"
              "// forward (fa_fwd_w64.hip) as gfx950 assembly, one string per element type, mask and\n"
