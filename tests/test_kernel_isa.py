@@ -139,3 +139,30 @@ def test_generated_key_loop_is_up_to_date():
         env = dict(os.environ, OUT_INC=out)
         subprocess.run([sys.executable, gen], check=True, env=env)
         assert open(out).read() == open(os.path.join(CSRC, "fa_fwd_kloop.inc")).read()
+
+
+def test_w64_compiler_code_leaves_m0_to_the_key_loop(w64_asm):
+    """The key loop's inline assembly sets m0 (the LDS address of its DMA loads) and lists it
+    among its clobbers, which the compiler ignores for this reserved register (it warns so).
+    That is safe only while the code the compiler writes around the assembly never reads or
+    writes m0: no instruction outside the asm blocks of any instantiation may name it."""
+    found = 0
+    for name in re.findall(r"^(_ZN2fa14fwd_w64_kernel\S+):", w64_asm, re.M):
+        found += 1
+        i = w64_asm.index(name + ":")
+        j = w64_asm.index(".Lfunc_end", i)
+        inside, asm_m0 = False, 0
+        for line in w64_asm[i:j].splitlines():
+            s = line.strip()
+            if s.startswith(";;#ASMSTART"):
+                inside = True
+                continue
+            if s.startswith(";;#ASMEND"):
+                inside = False
+                continue
+            if not s or s.startswith((";", ".")) or not re.search(r"\bm0\b", s):
+                continue
+            assert inside, (name, s)
+            asm_m0 += 1
+        assert asm_m0 > 0, name            # the key loop does use m0
+    assert found == 16
