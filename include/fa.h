@@ -43,9 +43,11 @@
  * q, k and v are only read; o and lse must not overlap the inputs or each other.
  * Every pointer must be 16-byte aligned.
  *
- * Errors: a return value other than FA_OK means nothing was enqueued.  Argument
- * errors are found on the host before any HIP call.  FA_ERR_HIP reports a
- * failed launch; fa_last_error() then holds the HIP message (thread-local).
+ * Errors: FA_ERR_INVALID_ARG and FA_ERR_UNSUPPORTED mean nothing was enqueued:
+ * arguments are checked on the host before any HIP call.  FA_ERR_HIP reports a
+ * failed launch; fa_last_error() then holds the HIP message (thread-local).  A
+ * call that launches several kernels (the backward; a row softmax of more than
+ * 2^23 rows, launched in pieces) may have enqueued the ones before it.
  * The call is asynchronous: faults during execution show at the caller's next
  * synchronisation of the stream.  No global mutable state beyond the
  * thread-local message: calls are re-entrant and may run on several streams and
